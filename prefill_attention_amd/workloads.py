@@ -1,0 +1,121 @@
+"""Seeded synthetic workloads for causal prefill attention.
+
+Holds none of the method's arithmetic: only the shapes of the workloads and
+the seeded draws of their inputs.  Both sides of every parity test (the HIP
+path and the CPU oracle) take their inputs from here.
+
+The pages measure a 7B model's prefill (head_dim 128; a 2659-token anchor
+prompt; 4 key/value heads — "28 · r23 — f16-path whole-graph wall
+decomposition", Result and §5.1; "53 · r50 — FA_TKV 32→16", §2).  Neither
+the model, its weights nor its prompts are available, and the pages publish
+no activation statistics, so N(0, 1) draws rounded to f16 stand in for the
+projected Q/K/V activations at those shapes.
+
+Recipe (per workload, from one CPU generator seeded with ``seed``):
+    q = f16(randn([S, n_q_heads, 128]))
+    k = f16(k_mult * randn([S, n_kv_heads, 128]))     (k_mult = 3 for the GQA case)
+    v = f16(randn([S, n_kv_heads, 128]))
+drawn in that order.  scale = float32(1 / sqrt(128)).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+HEAD_DIM = 128
+SCALE = float(np.float32(1.0 / math.sqrt(HEAD_DIM)))
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    name: str
+    n_q_heads: int
+    n_kv_heads: int
+    seq_len: int
+    seed: int
+    k_mult: float = 1.0
+    causal: bool = True
+    head_dim: int = HEAD_DIM
+    # number of query rows per head the oracle checks (None: all rows)
+    oracle_rows: int | None = None
+
+    @property
+    def visible_pairs(self) -> int:
+        S = self.seq_len
+        return S * (S + 1) // 2 if self.causal else S * S
+
+    @property
+    def flop(self) -> int:
+        """Algorithmic FLOP: 2 FLOP per multiply-add, Q.K^T and P.V, visible pairs only."""
+        return 4 * self.head_dim * self.n_q_heads * self.visible_pairs
+
+    def describe(self) -> dict:
+        return {
+            "workload": self.name,
+            "n_q_heads": self.n_q_heads,
+            "n_kv_heads": self.n_kv_heads,
+            "seq_len": self.seq_len,
+            "head_dim": self.head_dim,
+            "causal": self.causal,
+            "dtype_in": "f16",
+            "dtype_out": "f32",
+        }
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", "tiny causal attention, 2 heads, S=256, hd=128", 2, 2, 256, seed=1),
+    "7b_2k": Workload("7b_2k", "7B-layer causal prefill, 32/32 heads, S=2048, hd=128", 32, 32, 2048, seed=2),
+    "7b_2659": Workload(
+        "7b_2659", "7B-layer causal prefill at the 2659-token anchor, 32/32 heads, hd=128", 32, 32, 2659, seed=3
+    ),
+    "gqa_4k": Workload(
+        "gqa_4k", "GQA causal prefill, 32 q / 8 kv heads, S=4096, hd=128, K x3", 32, 8, 4096, seed=4, k_mult=3.0
+    ),
+    "long_16k": Workload(
+        "long_16k", "long GQA causal prefill, 32 q / 8 kv heads, S=16384, hd=128", 32, 8, 16384, seed=5,
+        oracle_rows=256,
+    ),
+}
+
+# Workload the throughput figure is quoted on.
+HEADLINE = "7b_2659"
+
+
+def make_inputs(wl: Workload, seed: int | None = None, device: str = "cpu"):
+    """(q, k, v) f16 tensors [S, heads, hd] drawn as described in the module docstring."""
+    g = torch.Generator(device="cpu").manual_seed(wl.seed if seed is None else seed)
+    S, hd = wl.seq_len, wl.head_dim
+    q = torch.randn([S, wl.n_q_heads, hd], dtype=torch.float32, generator=g).half()
+    k = (wl.k_mult * torch.randn([S, wl.n_kv_heads, hd], dtype=torch.float32, generator=g)).half()
+    v = torch.randn([S, wl.n_kv_heads, hd], dtype=torch.float32, generator=g).half()
+    if device != "cpu":
+        q, k, v = q.to(device), k.to(device), v.to(device)
+    return q, k, v
+
+
+def make_custom_inputs(seq_len: int, n_q_heads: int, n_kv_heads: int, seed: int,
+                       head_dim: int = HEAD_DIM, k_mult: float = 1.0):
+    """Same recipe at an arbitrary shape (tail sweeps, edge cases)."""
+    wl = Workload("custom", "custom", n_q_heads, n_kv_heads, seq_len, seed, k_mult=k_mult, head_dim=head_dim)
+    return make_inputs(wl)
+
+
+def row_subset(seq_len: int, n_rows: int, seed: int) -> np.ndarray:
+    """Sorted query rows checked against the oracle on long sequences.
+
+    Always includes the rows at tile and sequence edges {0, 1, 63, 64, 127,
+    128, S-2, S-1}; the rest are drawn without replacement by a PCG64
+    generator seeded with ``seed + 1000``.  The same rows are used for every head.
+    """
+    fixed = sorted({r for r in (0, 1, 63, 64, 127, 128, seq_len - 2, seq_len - 1) if 0 <= r < seq_len})
+    if n_rows >= seq_len:
+        return np.arange(seq_len, dtype=np.int64)
+    rest = np.setdiff1d(np.arange(seq_len, dtype=np.int64), np.asarray(fixed, dtype=np.int64))
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    extra = rng.choice(rest, size=n_rows - len(fixed), replace=False)
+    return np.sort(np.concatenate([np.asarray(fixed, dtype=np.int64), extra]))
