@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Throughput of causal prefill attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7b_2659]
+
+One step = one fa_prefill launch over the whole workload (32 heads x 2659
+tokens x head_dim 128, causal, f16 in, f32 out by default), inputs resident in
+HBM.  W untimed steps, then K steps back to back on one stream, bracketed by
+HIP events and device synchronisation.  Prints one JSON line.
+
+The reported throughput counts algorithmic FLOP only: 4 * head_dim per
+visible (query, key) pair per query head (Q.K^T and P.V multiply-adds, x2),
+not the masked upper triangle nor the padding of diagonal and tail tiles.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published dense f16 matrix peak: 256 CUs x 4096 FLOP/clk x 2.4 GHz.
+PEAK_F16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("prefill_attention_amd/csrc/fa_prefill.hip", "prefill_attention_amd/csrc/fa_geometry.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_prefill_kernel_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None.
+
+    Valid only for the kernel source they were taken on (hash recorded with
+    the numbers) and for the same workload.
+    """
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("workload") != workload_key:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, q, k, v, gpu_out, scale, budget_s: float = 12.0) -> dict:
+    """Time the float64 oracle on whole heads of the workload, about budget_s of CPU work."""
+    import numpy as np
+    from oracle import attention_f64, parity_errors
+
+    try:
+        import threadpoolctl
+
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                      if i.get("user_api") == "blas")
+    except Exception:  # threadpoolctl absent: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+    group = wl.n_q_heads // wl.n_kv_heads
+    heads, t_used, worst = 0, 0.0, 0.0
+    gpu_np = gpu_out.cpu().numpy()
+    while heads < wl.n_q_heads and t_used < budget_s:
+        h = heads
+        hk = h // group
+        t0 = time.perf_counter()
+        ref = attention_f64(q[:, h:h + 1], k[:, hk:hk + 1], v[:, hk:hk + 1], scale, wl.causal)
+        t_used += time.perf_counter() - t0
+        worst = max(worst, parity_errors(gpu_np[:, h:h + 1], ref)["max_abs"])
+        heads += 1
+    flop = 4 * wl.head_dim * heads * wl.visible_pairs
+    return {
+        "value": flop / t_used / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {heads} of {wl.n_q_heads} query heads, all {wl.seq_len} rows "
+                  f"({flop / 1e9:.2f} GFLOP algorithmic) in {t_used:.1f} s; numpy float64, "
+                  f"dense score matrix then mask",
+        "seconds": round(t_used, 3),
+        "gpu_vs_oracle_max_abs_on_sample": worst,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload key (default: the headline one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this library runs on one GPU; multi-GPU runs are not supported "
+              "(attention shards over heads with no exchange, but no multi-GPU path is built)",
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import prefill_attention_amd as fa
+    from prefill_attention_amd.workloads import HEADLINE, SCALE, WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    key = args.workload or HEADLINE
+    wl = WORKLOADS[key]
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    q, k, v = make_inputs(wl)
+    dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty((wl.seq_len, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    plan = fa.fa_prefill_plan(wl.n_q_heads, wl.n_kv_heads, wl.seq_len, wl.head_dim, int(wl.causal))
+
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            fa.attention(dq, dk, dv, SCALE, wl.causal, out=out, stream=stream)
+        stream.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            fa.attention(dq, dk, dv, SCALE, wl.causal, out=out, stream=stream)
+        end.record(stream)
+        end.synchronize()
+        torch.cuda.synchronize()
+    region_ms = start.elapsed_time(end)
+    ms_per_step = region_ms / args.steps
+    tflops = wl.flop / (ms_per_step * 1e-3) / 1e12
+
+    traffic = measured_traffic(key)
+    min_bytes = (q.numel() + k.numel() + v.numel()) * 2 + out.numel() * 4
+    line = {
+        "metric": "causal FA prefill TFLOP/s + % f16 MFMA peak (S=2659, 32 heads, hd=128)"
+        if key == HEADLINE else f"causal FA prefill TFLOP/s ({wl.name})",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {**wl.describe(), "workload_key": key, "plan": plan.as_dict()},
+        "pct_peak": round(100.0 * tflops / PEAK_F16_TFLOPS, 2),
+        "peak_basis": "MI355X dense f16 MFMA 256 CU x 4096 FLOP/clk x 2.4 GHz = 2516.6 TFLOP/s",
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": round(PEAK_F16_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_F16_TFLOPS, 4),
+            "traffic": traffic,
+            "flop_per_launch": wl.flop,
+            "avg_launch_us": round(ms_per_step * 1e3, 3),
+            "min_hbm_bytes_per_launch": min_bytes,
+            "kernel_source_hash": kernel_source_hash(),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, q, k, v, out, SCALE)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,120 @@
+/*
+ * fa_prefill.h — C ABI of the MI355X (gfx950) causal prefill flash-attention
+ * library, libfa_prefill.so.
+ *
+ * Operation.  For one sequence of seq_len tokens,
+ *
+ *     out[i, h, :] = sum_j softmax_j( scale * q[i, h, :] . k[j, hk, :] ) * v[j, hk, :]
+ *
+ * over the keys j visible from query i: with causal != 0, j <= i (the
+ * diagonal is visible) and j < seq_len; otherwise every j < seq_len.  This
+ * is the prefill attention of the pages' fa_prefill_f16kv kernel: tiled
+ * flash-attention with an online softmax ("49 · r46 (FAP1) — FA audit",
+ * §2.1) whose result equals the plain softmax at infinite precision ("53 ·
+ * r50 — FA_TKV 32→16 occupancy experiment", §2), under the validity
+ * predicate "key <= query position and key inside the stored sequence"
+ * ("28 · r23 — f16-path whole-graph wall decomposition", §2.3 and §3.2).
+ * Grouped-query attention uses consecutive groups: query head h reads
+ * key/value head hk = h / (n_q_heads / n_kv_heads).
+ *
+ * Precision.  f16 inputs, f32 accumulation in the matrix cores, the softmax
+ * in f32 registers, probabilities rounded to f16 (round to nearest even) as
+ * the operand of P.V, f32 output.
+ *
+ * Layout.  All tensors are dense, token-major, row-major:
+ *     q   f16 [seq_len][n_q_heads][head_dim]
+ *     k   f16 [seq_len][n_kv_heads][head_dim]
+ *     v   f16 [seq_len][n_kv_heads][head_dim]
+ *     out f32 [seq_len][n_q_heads][head_dim]
+ * (so one token's row of one head is head_dim contiguous elements).
+ *
+ * Ownership.  q, k, v and out are device memory owned by the caller; the
+ * library keeps no reference after the call returns and allocates nothing.
+ * out must not overlap q, k or v.
+ *
+ * Execution.  fa_prefill enqueues one kernel on `stream` (a hipStream_t;
+ * NULL = the null stream) and returns without waiting; the caller
+ * synchronises.  Only rows i < seq_len of out are written.
+ *
+ * Errors.  Every function returns an fa_status; no call falls back to
+ * another code path.  Argument errors are detected on the host before any
+ * GPU call.  fa_prefill_last_error() gives a detail message for the last
+ * failing call on the calling thread.
+ */
+#ifndef FA_PREFILL_H
+#define FA_PREFILL_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,            /* success (seq_len == 0 is a successful no-op)         */
+    FA_ERR_NULL = 1,      /* q, k, v or out is NULL (with seq_len > 0)             */
+    FA_ERR_SHAPE = 2,     /* seq_len < 0, heads <= 0, n_q_heads % n_kv_heads != 0,
+                             or a size that overflows the launch grid              */
+    FA_ERR_HEAD_DIM = 3,  /* head_dim != 128                                       */
+    FA_ERR_SCALE = 4,     /* scale is NaN or infinite                              */
+    FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                      */
+    FA_ERR_RESOURCE = 6,  /* the launch plan exceeds a device limit (LDS bytes)     */
+    FA_ERR_LAUNCH = 7,    /* the HIP runtime reported an error at launch           */
+    FA_ERR_ALIAS = 8,     /* out overlaps q, k or v                                */
+    FA_ERR_DEVICE = 9     /* no usable device, or the device is not gfx950         */
+} fa_status;
+
+/* The only head dimension the kernel is built for (the pages' model uses
+ * head_dim 128 throughout). */
+#define FA_HEAD_DIM 128
+
+/* Launch plan of one fa_prefill call: pure host arithmetic, no GPU needed. */
+typedef struct fa_plan {
+    int q_tile;              /* query rows per work-group                         */
+    int kv_tile;             /* key/value rows per LDS tile                       */
+    int waves_per_group;     /* 64-lane wavefronts per work-group                 */
+    int threads_per_group;   /* waves_per_group * 64                              */
+    int n_q_tiles;           /* ceil(seq_len / q_tile)                            */
+    long long n_groups;      /* work-groups launched: n_q_tiles * n_q_heads       */
+    int lds_bytes;           /* LDS per work-group: the sum of its planes         */
+    int lds_k_bytes;         /* K tile plane  [kv_tile][head_dim + pad] f16        */
+    int lds_vt_bytes;        /* V^T tile plane [head_dim][kv_tile + pad] f16       */
+    long long kv_tiles_visited; /* KV tiles the grid visits (causal tiles skipped) */
+} fa_plan;
+
+/*
+ * Enqueue causal (or full) prefill attention.
+ *   q, k, v    device pointers, f16, layouts above, 16-byte aligned
+ *   out        device pointer, f32 [seq_len][n_q_heads][head_dim], 16-byte aligned
+ *   n_q_heads  >= 1, a multiple of n_kv_heads
+ *   n_kv_heads >= 1
+ *   seq_len    >= 0 (0: nothing is launched, FA_OK)
+ *   head_dim   must be FA_HEAD_DIM
+ *   scale      finite; multiplies q.k (typically 1/sqrt(head_dim))
+ *   causal     0: every key visible; nonzero: key j visible from query i iff j <= i
+ *   stream     hipStream_t to enqueue on (NULL: the null stream)
+ * Returns FA_OK or an fa_status error; nothing is enqueued on error.
+ */
+int fa_prefill(const void* q, const void* k, const void* v, float* out,
+               int n_q_heads, int n_kv_heads, int seq_len, int head_dim,
+               float scale, int causal, void* stream);
+
+/*
+ * Compute the launch plan fa_prefill would use, without touching the GPU.
+ * Validates the shape arguments exactly as fa_prefill does (pointers aside).
+ * max_lds_bytes: the device's LDS limit per work-group (0 = do not check).
+ * plan: caller-owned output, written on FA_OK.
+ */
+int fa_prefill_plan(int n_q_heads, int n_kv_heads, int seq_len, int head_dim,
+                    int causal, int max_lds_bytes, fa_plan* plan);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_prefill_strerror(int status);
+
+/* Detail of the last error on the calling thread ("" if none); valid until the
+ * next call into the library from the same thread. */
+const char* fa_prefill_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_PREFILL_H */

@@ -1,1 +1,29 @@
-"""MI355X-native causal prefill flash-attention (gfx950 HIP kernel behind a C ABI)."""
+"""MI355X-native causal prefill flash-attention (gfx950 HIP kernel behind a C ABI).
+
+The compute runs only in ``libfa_prefill.so``; ``binding`` marshals torch
+tensors to its C entry points (same names as in include/fa_prefill.h).
+"""
+
+from .binding import (
+    EXPORTED,
+    FaError,
+    FaPlan,
+    attention,
+    fa_prefill,
+    fa_prefill_last_error,
+    fa_prefill_plan,
+    fa_prefill_strerror,
+    load_library,
+)
+
+__all__ = [
+    "EXPORTED",
+    "FaError",
+    "FaPlan",
+    "attention",
+    "fa_prefill",
+    "fa_prefill_last_error",
+    "fa_prefill_plan",
+    "fa_prefill_strerror",
+    "load_library",
+]

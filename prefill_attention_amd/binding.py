@@ -1,0 +1,161 @@
+"""ctypes binding of libfa_prefill.so — argument marshalling only.
+
+Every step of the attention runs in the HIP library; this module only turns
+torch tensors into device pointers and forwards them.  There is no CPU or
+PyTorch fallback: if the library is missing or the call fails, it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_prefill.so")
+
+FA_OK = 0
+STATUS_NAMES = {
+    0: "FA_OK",
+    1: "FA_ERR_NULL",
+    2: "FA_ERR_SHAPE",
+    3: "FA_ERR_HEAD_DIM",
+    4: "FA_ERR_SCALE",
+    5: "FA_ERR_ALIGN",
+    6: "FA_ERR_RESOURCE",
+    7: "FA_ERR_LAUNCH",
+    8: "FA_ERR_ALIAS",
+    9: "FA_ERR_DEVICE",
+}
+# Every symbol include/fa_prefill.h declares.
+EXPORTED = ("fa_prefill", "fa_prefill_plan", "fa_prefill_strerror", "fa_prefill_last_error")
+
+
+class FaPlan(ctypes.Structure):
+    """Mirror of ``struct fa_plan``."""
+
+    _fields_ = [
+        ("q_tile", ctypes.c_int),
+        ("kv_tile", ctypes.c_int),
+        ("waves_per_group", ctypes.c_int),
+        ("threads_per_group", ctypes.c_int),
+        ("n_q_tiles", ctypes.c_int),
+        ("n_groups", ctypes.c_longlong),
+        ("lds_bytes", ctypes.c_int),
+        ("lds_k_bytes", ctypes.c_int),
+        ("lds_vt_bytes", ctypes.c_int),
+        ("kv_tiles_visited", ctypes.c_longlong),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa_prefill.so once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise FileNotFoundError(
+                f"{path} is missing: build it with `python -m prefill_attention_amd.build` "
+                "(there is no fallback implementation)"
+            )
+        lib = ctypes.CDLL(path)
+        lib.fa_prefill.restype = ctypes.c_int
+        lib.fa_prefill.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
+        ]
+        lib.fa_prefill_plan.restype = ctypes.c_int
+        lib.fa_prefill_plan.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.POINTER(FaPlan),
+        ]
+        lib.fa_prefill_strerror.restype = ctypes.c_char_p
+        lib.fa_prefill_strerror.argtypes = [ctypes.c_int]
+        lib.fa_prefill_last_error.restype = ctypes.c_char_p
+        lib.fa_prefill_last_error.argtypes = []
+        _lib = lib
+        return lib
+
+
+def _check(status: int) -> None:
+    if status != FA_OK:
+        lib = load_library()
+        detail = lib.fa_prefill_last_error().decode() or lib.fa_prefill_strerror(status).decode()
+        raise FaError(status, detail)
+
+
+def fa_prefill(q, k, v, out, n_q_heads: int, n_kv_heads: int, seq_len: int, head_dim: int,
+               scale: float, causal: int, stream) -> int:
+    """Same arguments as the C function; pointers as ints (or None), returns the status."""
+    lib = load_library()
+    return lib.fa_prefill(q, k, v, out, int(n_q_heads), int(n_kv_heads), int(seq_len),
+                          int(head_dim), float(scale), int(causal), stream)
+
+
+def fa_prefill_plan(n_q_heads: int, n_kv_heads: int, seq_len: int, head_dim: int, causal: int,
+                    max_lds_bytes: int = 0) -> FaPlan:
+    """Launch plan (no GPU); raises FaError on invalid shapes."""
+    lib = load_library()
+    plan = FaPlan()
+    _check(lib.fa_prefill_plan(int(n_q_heads), int(n_kv_heads), int(seq_len), int(head_dim),
+                               int(causal), int(max_lds_bytes), ctypes.byref(plan)))
+    return plan
+
+
+def fa_prefill_strerror(status: int) -> str:
+    return load_library().fa_prefill_strerror(int(status)).decode()
+
+
+def fa_prefill_last_error() -> str:
+    return load_library().fa_prefill_last_error().decode()
+
+
+def attention(q, k, v, scale: float, causal: bool = True, out=None, stream=None):
+    """Torch-facing call: q [S, Hq, 128] f16, k/v [S, Hkv, 128] f16 on one GPU.
+
+    Allocates ``out`` (f32 [S, Hq, 128]) unless given, enqueues the kernel on
+    ``stream`` (default: torch's current stream) and returns ``out``.
+    """
+    import torch
+
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [seq_len, heads, head_dim]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.float16:
+            raise TypeError(f"{name} must be float16, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    S, n_q, hd = q.shape
+    if k.shape != v.shape or k.shape[0] != S or k.shape[2] != hd:
+        raise ValueError("k and v must be [seq_len, n_kv_heads, head_dim] matching q")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on the same device")
+    if out is None:
+        out = torch.empty((S, n_q, hd), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or out.shape != (S, n_q, hd) or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be contiguous float32 [seq_len, n_q_heads, head_dim] on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    with torch.cuda.device(q.device):
+        status = fa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), n_q,
+                            k.shape[1], S, hd, scale, 1 if causal else 0, handle)
+    _check(status)
+    return out

@@ -1,0 +1,207 @@
+"""GPU parity: the HIP kernel (through the C ABI) against the CPU float64 oracle.
+
+Bar: max-abs error <= 2e-3 and floored relative error <= 1e-2 on every element
+the oracle computes (f16 inputs, f32 accumulation, f32 output).  The long
+workload is compared on a seeded subset of 256 query rows per head, at the
+full size and in the launch configuration the benchmark times.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention_f64, parity_errors, within_tolerance
+from oracle.attention import attention_rows_blocked
+from prefill_attention_amd.workloads import SCALE, WORKLOADS, make_custom_inputs, make_inputs, row_subset
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import prefill_attention_amd as fa_mod
+
+    fa_mod.load_library()  # raises if the HIP library is not built
+    return fa_mod
+
+
+def _run(fa, q, k, v, scale=SCALE, causal=True):
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    out = fa.attention(dq, dk, dv, scale, causal)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _report(tag, err):
+    print(f"[parity] {tag}: max_abs={err['max_abs']:.3e} max_rel={err['max_rel']:.3e} "
+          f"normwise={err['normwise']:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("key", ["tiny", "7b_2k", "7b_2659", "gqa_4k"])
+def test_workload_full_parity(fa, key):
+    wl = WORKLOADS[key]
+    q, k, v = make_inputs(wl)
+    got = _run(fa, q, k, v)
+    ref = attention_rows_blocked(q, k, v, SCALE, True, block=1024)
+    err = parity_errors(got, ref)
+    _report(key, err)
+    assert within_tolerance(err), err
+
+
+@pytest.mark.parametrize("key", ["tiny", "7b_2k", "7b_2659"])
+def test_workload_second_seed(fa, key):
+    wl = WORKLOADS[key]
+    q, k, v = make_inputs(wl, seed=wl.seed + 100)
+    got = _run(fa, q, k, v)
+    rows = row_subset(wl.seq_len, 384, seed=wl.seed + 100)
+    ref = attention_f64(q, k, v, SCALE, True, rows=rows)
+    err = parity_errors(got[rows], ref)
+    _report(f"{key}/seed+100", err)
+    assert within_tolerance(err), err
+
+
+def test_long_16k_sampled_rows(fa):
+    wl = WORKLOADS["long_16k"]
+    q, k, v = make_inputs(wl)
+    got = _run(fa, q, k, v)
+    assert np.all(np.isfinite(got))
+    rows = row_subset(wl.seq_len, wl.oracle_rows, seed=wl.seed)
+    ref = attention_rows_blocked(q, k, v, SCALE, True, rows=rows, block=64)
+    err = parity_errors(got[rows], ref)
+    _report("long_16k (256 rows/head)", err)
+    assert within_tolerance(err), err
+
+
+TAIL_LENGTHS = [1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 95, 127, 128, 129, 191, 255, 257, 300]
+
+
+@pytest.mark.parametrize("S", TAIL_LENGTHS)
+@pytest.mark.parametrize("heads", [(2, 1), (3, 3)])
+def test_tail_sweep_causal(fa, S, heads):
+    n_q, n_kv = heads
+    q, k, v = make_custom_inputs(S, n_q, n_kv, seed=1000 + S)
+    err = parity_errors(_run(fa, q, k, v), attention_f64(q, k, v, SCALE, True))
+    assert within_tolerance(err), (S, heads, err)
+
+
+@pytest.mark.parametrize("S", [1, 17, 64, 65, 200, 256])
+def test_non_causal(fa, S):
+    q, k, v = make_custom_inputs(S, 4, 2, seed=2000 + S)
+    err = parity_errors(_run(fa, q, k, v, causal=False), attention_f64(q, k, v, SCALE, False))
+    assert within_tolerance(err), (S, err)
+
+
+def test_non_causal_tiny_workload(fa):
+    q, k, v = make_inputs(WORKLOADS["tiny"])
+    err = parity_errors(_run(fa, q, k, v, causal=False), attention_f64(q, k, v, SCALE, False))
+    _report("tiny non-causal", err)
+    assert within_tolerance(err), err
+
+
+@pytest.mark.parametrize("scale", [0.0, -SCALE, 0.5, 1e-3])
+def test_other_scales(fa, scale):
+    q, k, v = make_custom_inputs(150, 2, 2, seed=77)
+    for causal in (True, False):
+        err = parity_errors(_run(fa, q, k, v, scale=scale, causal=causal),
+                            attention_f64(q, k, v, scale, causal))
+        assert within_tolerance(err), (scale, causal, err)
+
+
+def test_query0_returns_v0_bit_exact(fa):
+    q, k, v = make_custom_inputs(300, 4, 2, seed=5)
+    got = _run(fa, q, k, v)
+    v0 = v[0].float().numpy().astype(np.float64)
+    for h in range(4):
+        assert np.array_equal(got[0, h], v0[h // 2])
+
+
+def test_constant_v_returns_constant(fa):
+    q, k, _ = make_custom_inputs(333, 4, 4, seed=6)
+    c = torch.linspace(-2, 2, 128).half()
+    v = c.view(1, 1, 128).expand(333, 4, 128).contiguous()
+    got = _run(fa, q, k, v)
+    assert np.max(np.abs(got - c.float().numpy()[None, None, :])) <= 1e-5
+
+
+def test_zero_q_gives_prefix_mean(fa):
+    _, k, v = make_custom_inputs(260, 2, 2, seed=8)
+    q = torch.zeros(260, 2, 128, dtype=torch.float16)
+    got = _run(fa, q, k, v)
+    vf = v.float().numpy().astype(np.float64)
+    prefix = np.cumsum(vf, axis=0) / np.arange(1, 261)[:, None, None]
+    assert np.max(np.abs(got - prefix)) <= 2e-3
+
+
+def test_gqa_mapping_distinct_constant_v(fa):
+    q, k, _ = make_custom_inputs(130, 8, 2, seed=9)
+    v = torch.empty(130, 2, 128, dtype=torch.float16)
+    v[:, 0], v[:, 1] = 1.0, -3.0
+    got = _run(fa, q, k, v)
+    assert np.max(np.abs(got[:, :4] - 1.0)) <= 1e-5
+    assert np.max(np.abs(got[:, 4:] + 3.0)) <= 1e-5
+
+
+def test_head_dim_slices(fa):
+    """Q/K nonzero in one 16-wide head-dim slice only: catches operand k-offset mistakes."""
+    S = 190
+    for lo in (0, 16, 48, 112):
+        q, k, v = make_custom_inputs(S, 2, 1, seed=40 + lo, k_mult=2.0)
+        mask = torch.zeros(128, dtype=torch.bool)
+        mask[lo:lo + 16] = True
+        q = torch.where(mask, q, torch.zeros_like(q))
+        k = torch.where(mask, k, torch.zeros_like(k))
+        err = parity_errors(_run(fa, q, k, v), attention_f64(q, k, v, SCALE, True))
+        assert within_tolerance(err), (lo, err)
+
+
+def test_guard_band_untouched_and_rerun_identical(fa):
+    S, n_q = 259, 4
+    q, k, v = make_custom_inputs(S, n_q, 1, seed=10)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    buf = torch.full((S + 64, n_q, 128), float("nan"), dtype=torch.float32, device="cuda")
+    out = buf[:S]
+    fa.attention(dq, dk, dv, SCALE, True, out=out)
+    first = out.clone()
+    fa.attention(dq, dk, dv, SCALE, True, out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[S:]).all().item(), "rows past seq_len were written"
+    assert torch.equal(first, out), "reruns differ"
+    err = parity_errors(out.cpu().numpy(), attention_f64(q, k, v, SCALE, True))
+    assert within_tolerance(err), err
+
+
+def test_side_stream(fa):
+    q, k, v = make_custom_inputs(200, 2, 2, seed=11)
+    s = torch.cuda.Stream()
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out = fa.attention(dq, dk, dv, SCALE, True, stream=s)
+    s.synchronize()
+    err = parity_errors(out.cpu().numpy(), attention_f64(q, k, v, SCALE, True))
+    assert within_tolerance(err), err
+
+
+def test_seq_len_zero_is_noop(fa):
+    q = torch.empty(0, 2, 128, dtype=torch.float16, device="cuda")
+    out = fa.attention(q, q[:, :1], q[:, :1], SCALE, True)
+    assert out.shape == (0, 2, 128)
+
+
+def test_error_paths_on_device(fa):
+    q, k, v = (t.cuda() for t in make_custom_inputs(64, 2, 2, seed=12))
+    out = torch.empty(64, 2, 128, dtype=torch.float32, device="cuda")
+    # misaligned output pointer
+    st = fa.fa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr() + 4, 2, 2, 63, 128,
+                       SCALE, 1, None)
+    assert st == 5
+    # output aliasing an input
+    st = fa.fa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), k.data_ptr(), 2, 2, 64, 128,
+                       SCALE, 1, None)
+    assert st == 8
+    st = fa.fa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), 2, 2, 64, 128,
+                       float("nan"), 1, None)
+    assert st == 4
