@@ -74,9 +74,10 @@ typedef struct fa_plan {
     int threads_per_group;   /* waves_per_group * 64                              */
     int n_q_tiles;           /* ceil(seq_len / q_tile)                            */
     long long n_groups;      /* work-groups launched: n_q_tiles * n_q_heads       */
+    int stages;              /* K/V tiles resident in LDS at once (buffering)     */
     int lds_bytes;           /* LDS per work-group: the sum of its planes         */
-    int lds_k_bytes;         /* K tile plane  [kv_tile][head_dim + pad] f16        */
-    int lds_vt_bytes;        /* V^T tile plane [head_dim][kv_tile + pad] f16       */
+    int lds_k_bytes;         /* K planes: stages x [kv_tile][head_dim] f16        */
+    int lds_v_bytes;         /* V planes: stages x [kv_tile][head_dim] f16        */
     long long kv_tiles_visited; /* KV tiles the grid visits (causal tiles skipped) */
 } fa_plan;
 

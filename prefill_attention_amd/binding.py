@@ -40,9 +40,10 @@ class FaPlan(ctypes.Structure):
         ("threads_per_group", ctypes.c_int),
         ("n_q_tiles", ctypes.c_int),
         ("n_groups", ctypes.c_longlong),
+        ("stages", ctypes.c_int),
         ("lds_bytes", ctypes.c_int),
         ("lds_k_bytes", ctypes.c_int),
-        ("lds_vt_bytes", ctypes.c_int),
+        ("lds_v_bytes", ctypes.c_int),
         ("kv_tiles_visited", ctypes.c_longlong),
     ]
 

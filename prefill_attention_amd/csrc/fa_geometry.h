@@ -16,16 +16,17 @@ constexpr int kWaves = 4;              // wavefronts per work-group
 constexpr int kThreads = kWaves * kWaveSize;
 constexpr int kQTile = kWaves * kQRowsPerWave;  // 128 query rows per work-group
 constexpr int kKvTile = 64;            // key/value rows per LDS tile
+constexpr int kStages = 2;             // LDS tiles in flight (double buffer)
 
-// LDS planes (f16 elements).  K is stored as rows of head_dim, V transposed
-// as rows of kv_tile; the pads make consecutive rows start 16 bytes apart
-// modulo 128 bytes, so the eight 16-byte row fragments read by one group of
-// lanes fall on distinct banks.
-constexpr int kKStride = kHeadDim + 8;   // 136 halves = 272 B per key row
-constexpr int kVtStride = kKvTile + 8;   // 72 halves = 144 B per head-dim row
-constexpr int kLdsKBytes = kKvTile * kKStride * 2;
-constexpr int kLdsVtBytes = kHeadDim * kVtStride * 2;
-constexpr int kLdsBytes = kLdsKBytes + kLdsVtBytes;
+// LDS planes.  K and V tiles are both stored key-major with unpadded
+// 256-byte rows; the sixteen 16-byte chunks of a row are permuted by
+// chunk ^ swizzle(row) (see fa_prefill.hip), which keeps both the K operand
+// reads and the transposed V reads free of bank conflicts.
+constexpr int kRowBytes = kHeadDim * 2;
+constexpr int kTileBytes = kKvTile * kRowBytes;           // one K or one V tile: 16 KiB
+constexpr int kLdsKBytes = kStages * kTileBytes;
+constexpr int kLdsVBytes = kStages * kTileBytes;
+constexpr int kLdsBytes = kLdsKBytes + kLdsVBytes;       // 64 KiB
 
 // Work-groups are dispatched round-robin over the 8 XCDs of an MI355X.
 constexpr int kXcds = 8;

@@ -46,6 +46,10 @@ int make_plan(int n_q_heads, int n_kv_heads, int seq_len, int head_dim, int caus
     if (n_q_heads % n_kv_heads != 0)
         return fail(FA_ERR_SHAPE, "n_q_heads %d is not a multiple of n_kv_heads %d", n_q_heads,
                     n_kv_heads);
+    // a 64-row K/V tile of one head must be addressable with 31-bit buffer offsets
+    if ((long long)n_kv_heads * kRowBytes * kKvTile > INT_MAX)
+        return fail(FA_ERR_SHAPE, "n_kv_heads %d too large (row stride overflows buffer offsets)",
+                    n_kv_heads);
     if (head_dim != kHeadDim)
         return fail(FA_ERR_HEAD_DIM, "head_dim %d unsupported (only %d)", head_dim, kHeadDim);
     long long n_q_tiles = ((long long)seq_len + kQTile - 1) / kQTile;
@@ -65,9 +69,10 @@ int make_plan(int n_q_heads, int n_kv_heads, int seq_len, int head_dim, int caus
         plan->threads_per_group = kThreads;
         plan->n_q_tiles = (int)n_q_tiles;
         plan->n_groups = n_groups;
+        plan->stages = kStages;
         plan->lds_bytes = kLdsBytes;
         plan->lds_k_bytes = kLdsKBytes;
-        plan->lds_vt_bytes = kLdsVtBytes;
+        plan->lds_v_bytes = kLdsVBytes;
         long long tiles = 0;
         for (long long t = 0; t < n_q_tiles; ++t)
             tiles += tiles_for_group((int)(t * kQTile), seq_len, causal != 0);

@@ -11,8 +11,21 @@
 //
 //  * A work-group of 4 wavefronts owns 128 query rows of one head; each
 //    wavefront owns 32 of them.  It walks the key/value sequence in tiles of
-//    64 rows staged in LDS, and stops at the causal bound, so tiles above the
-//    diagonal are never visited (the pages' KV loop bound, "53 · r50", §3.2).
+//    64 rows and stops at the causal bound, so tiles above the diagonal are
+//    never visited (the pages' KV loop bound, "53 · r50", §3.2).
+//
+//  * K and V tiles go from HBM/L2 straight into LDS with buffer loads that
+//    write LDS directly (no register staging).  The buffer descriptor's
+//    record count ends at the sequence end, so rows past seq_len read as
+//    zeros in hardware (the pages zero-fill them explicitly, "53 · r50", §2).
+//    Two LDS stages: tile j+1 streams in while tile j is computed, with one
+//    work-group barrier per tile.
+//
+//  * LDS rows are the unpadded 256-byte K/V rows; the 16-byte chunk c of key
+//    row r is stored at chunk c ^ swz(r).  This replaces the pages' +8-half
+//    row padding ("11 · P5 — prefill gap session", §2.2) because the
+//    direct-to-LDS loads write 1 KiB contiguously per instruction, and it
+//    keeps both read patterns below free of bank conflicts.
 //
 //  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_f16:
 //    K (from LDS) is the A operand, Q^T (registers, loaded once) is B.  In the
@@ -22,13 +35,11 @@
 //    v_permlane32_swap, and the probabilities of a lane are already laid out
 //    as the B operand (k = key, n = query) of O^T = V^T P^T.  P never leaves
 //    the registers (the register-resident softmax idea of the pages' FAP2,
-//    "49 · r46", §5, and "11 · P5 — prefill gap session", §3.2, re-derived
-//    for the CDNA accumulator layout).
+//    "49 · r46", §5, and "11 · P5", §3.2, re-derived for the CDNA layout).
 //
-//  * V is staged transposed (V^T: rows = head-dim, columns = keys) so the A
-//    operand of O^T = V^T P^T is one 16-byte LDS read per lane.  The keys of
-//    a tile are stored with bits 2 and 3 of the key index swapped, which
-//    puts the 8 keys a lane's probability registers hold side by side.
+//  * The A operand of O^T = V^T P^T (head-dim x keys) is read from the
+//    key-major V tile with ds_read_b64_tr_b16, whose 16-lane transpose turns
+//    four 8-byte row pieces into four keys of one head-dim column per lane.
 //
 //  * Softmax in base 2: p = 2^(s*scale*log2(e) - m).  The running reference
 //    m is only raised when a tile's maximum exceeds it by more than 8 (log2
@@ -39,8 +50,7 @@
 //  * The validity predicate is "key <= query (causal) and key < seq_len",
 //    both bounds always applied (the pages' tail-tile lane-mask bug, "28 ·
 //    r23", §2.3), but only on tiles that touch the diagonal or the sequence
-//    end; every other tile runs unmasked.  Key/value rows past seq_len are
-//    staged as zeros.
+//    end; every other tile runs unmasked.
 //
 //  * Work-group order: the heaviest query tiles first; when the head count is
 //    a multiple of 8, the 8 XCDs (which receive work-groups round-robin) each
@@ -59,24 +69,37 @@ namespace fa {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) short4v lds_short4;
 
 // Lazy-rescale threshold in log2 units: probabilities stay <= 2^8.
 constexpr float kTau = 8.0f;
+// Buffer descriptor word 3 for raw (untyped) dword access on CDNA.
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// Chunk permutation of key row r: ((r & 3) << 2) | ((r >> 2) & 3).  Sixteen
+// consecutive rows map one logical chunk to 16 distinct chunks (the K
+// operand reads: 16 lanes x 16 B); four consecutive rows map four
+// neighbouring chunks to 16 distinct chunks (the transposed V reads: 32
+// lanes x 8 B cover 4 rows x 64 B), so neither read pattern has a bank
+// conflict on 64 banks of 4 bytes.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 // max / sum of x over the lane pair (lane, lane ^ 32).  v_permlane32_swap
 // exchanges the upper half of its first operand with the lower half of its
-// second; with both operands = x the two results hold x and x of the
-// partner lane, in some order, in every lane.
+// second; with both operands = x the two results hold x and the partner
+// lane's x, in some order, in every lane.
 __device__ __forceinline__ float pair_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -92,102 +115,201 @@ __device__ __forceinline__ int acc_key(int kb, int i, int g) {
     return 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
 }
 
-// One 64-key tile for the 32 queries of this wavefront.
-template <bool MASKED, bool CAUSAL>
-__device__ __forceinline__ void tile_step(const _Float16* __restrict__ Ks,
-                                          const _Float16* __restrict__ Vt, const half8 (&qb)[8],
-                                          floatx16 (&oacc)[4], float& m_ref, float& l_part, int kt,
-                                          int qw, int my_q, int seq_len, float c2, int l32, int g) {
-    // Second 32-key block needed at all?  (Only tiles on the diagonal or at
-    // the sequence end can skip it.)
-    const bool blk1 =
-        !MASKED || ((kt + 32 < seq_len) && (!CAUSAL || kt + 32 <= qw + kQRowsPerWave - 1));
-
-    // S^T = K Q^T over head_dim = 8 x 16.
-    floatx16 s0 = {}, s1 = {};
-    const _Float16* kp = Ks + l32 * kKStride + 8 * g;
+// Copy key/value rows [kt, kt + 64) of head hk from src (f16 [S][n_kv][128])
+// into an LDS tile; this wavefront copies rows 16*wave .. 16*wave + 15, four
+// rows (1 KiB) per instruction.  Lane i of an instruction fills physical
+// chunk i % 16 of its row, so it loads logical chunk (i % 16) ^ swz(row).
+__device__ __forceinline__ void stage_tile(const _Float16* __restrict__ src, int n_kv, int hk,
+                                           int seq_len, int kt, char* tile, int wave, int lane) {
+    const uint32_t row_bytes = (uint32_t)n_kv * kRowBytes;
+    const char* base = reinterpret_cast<const char*>(src) + (size_t)kt * row_bytes +
+                       (size_t)hk * kRowBytes;
+    // Bytes addressable from base: up to the end of the last valid row of
+    // this head, so rows >= seq_len fall outside the record and read as 0.
+    const long long valid = (long long)(seq_len - kt) * row_bytes - (long long)hk * kRowBytes;
+    const long long cap = (long long)kKvTile * row_bytes;
+    const uint32_t n_records = (uint32_t)(valid < cap ? valid : cap);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)n_records, kBufferFlags);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-        s0 = mfma32(*reinterpret_cast<const half8*>(kp + 16 * t), qb[t], s0);
-    if (blk1) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            s1 = mfma32(*reinterpret_cast<const half8*>(kp + 32 * kKStride + 16 * t), qb[t], s1);
+    for (int j = 0; j < 4; ++j) {
+        const int row0 = 16 * wave + 4 * j;
+        const int row = row0 + (lane >> 4);
+        const int chunk = (lane & 15) ^ swz(row);
+        const uint32_t voff = (uint32_t)row * row_bytes + (uint32_t)chunk * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + row0 * kRowBytes), 16, voff,
+                                                 0, 0, 0);
     }
+}
 
-    auto valid = [&](int kb, int i) {
-        const int key = kt + acc_key(kb, i, g);
-        return key < seq_len && (!CAUSAL || key <= my_q);
-    };
-    if (MASKED) {
+// A operand of O^T += V^T P^T for head-dim block db and key step ks: the
+// 32 x 16 slice V^T[32db .. 32db+31][16ks .. 16ks+15] in the slot order of
+// the probability registers (slot (g, e) <-> key 16ks + 8(e/4) + 4g + e%4).
+// Two transposed reads: within each 16-lane group, lane i addresses row
+// i/4, head-dim columns 4(i%4) .. +3 of the group's 16 columns, and receives
+// column i of the four rows.
+__device__ __forceinline__ half8 load_vt(const char* vtile, int db, int ks, int l32, int g) {
+    const int i = l32 & 15;
+    const int r = i >> 2, qd = i & 3;
+    const int chunk = 4 * db + 2 * (l32 >> 4) + (qd >> 1);
+    half8 a;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int key = 16 * ks + 8 * h + 4 * g + r;
+        const char* p = vtile + key * kRowBytes + ((chunk ^ swz(key)) << 4) + ((qd & 1) << 3);
+        const short4v t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
+        const half4 hv = __builtin_bit_cast(half4, t);
+        a[4 * h + 0] = hv[0];
+        a[4 * h + 1] = hv[1];
+        a[4 * h + 2] = hv[2];
+        a[4 * h + 3] = hv[3];
+    }
+    return a;
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Scores of one 64-key tile for this wavefront's 32 queries: S^T blocks for
+// keys [0, 32) and [32, 64) of the tile.
+struct TileScores {
+    floatx16 b[2];
+};
+
+// Mask the scores of tile t: -inf where the key is past the sequence or (causal)
+// after the query.  Only tiles on the diagonal or at the sequence end need it.
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_scores(TileScores& s, int t, int my_q, int seq_len, int g) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            s0[i] = valid(0, i) ? s0[i] : -INFINITY;
-            s1[i] = valid(1, i) ? s1[i] : -INFINITY;
+            const int key = t * kKvTile + acc_key(kb, i, g);
+            const bool ok = key < seq_len && (!CAUSAL || key <= my_q);
+            s.b[kb][i] = ok ? s.b[kb][i] : -INFINITY;
         }
-    }
+}
 
-    // Tile row maximum of this query, in log2 units.
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int i = 1; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s0[i]), s0[i + 1]);
-#pragma unroll
-    for (int i = 1; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s1[i]), s1[i + 1]);
-    mx = pair_max(mx);
-    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
+template <bool CAUSAL>
+__device__ __forceinline__ bool tile_needs_mask(int t, int qw, int seq_len) {
+    return (t * kKvTile + kKvTile > seq_len) ||
+           (CAUSAL && t * kKvTile + kKvTile - 1 > qw);
+}
 
-    // Raise the reference only when some query's maximum outgrew it by > tau.
-    if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau)) {
-        const float m_new = fmaxf(m_ref, mt);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        m_ref = m_new;
-    }
-
-    // p = 2^(s*c2 - m), rounded to f16 as the B operand of O^T += V^T P^T;
-    // the row sum accumulates the same rounded values.
-    half8 pb[4];
+// Phase A of the tile pipeline.  VALU (when HAS_CUR): probabilities of the current tile,
+// p = 2^(s*c2 - m) rounded to f16 (the B operand of O^T += V^T P^T), and
+// their row sum.  MFMA (when HAS_NEXT): scores of the next tile, S^T = K Q^T,
+// with K read from LDS.  The two streams are independent, so they are
+// interleaved: one MFMA, one LDS read for a later MFMA, six VALU ops.
+template <bool HAS_CUR, bool HAS_NEXT>
+__device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next, const half8 (&qb)[8],
+                                        const TileScores& sc, TileScores& sn, half8 (&pb)[4],
+                                        float& l_part, float m_ref, float c2, int l32, int g) {
     float lsum = 0.0f;
     const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        if (kb == 1 && !blk1) {
-            pb[2] = half8{};
-            pb[3] = half8{};
-            break;
-        }
+    for (int kb = 0; kb < 2 && HAS_CUR; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-            const floatx16& s = kb ? s1 : s0;
-            float p0 = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -m_ref));
-            float p1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c2, -m_ref));
-            if (MASKED) {
-                p0 = valid(kb, i) ? p0 : 0.0f;
-                p1 = valid(kb, i + 1) ? p1 : 0.0f;
-            }
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc.b[kb][i], c2, -m_ref));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc.b[kb][i + 1], c2, -m_ref));
             const floatx2 pf = {p0, p1};
             const half2v ph = __builtin_convertvector(pf, half2v);
             pb[2 * kb + (i >> 3)][i & 7] = ph[0];
             pb[2 * kb + (i >> 3)][(i & 7) + 1] = ph[1];
             lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
         }
+    if (HAS_NEXT) {
+        // K fragment t of block kb: key row 32kb + l32, head-dim 16t + 8g.
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int row = 32 * kb + l32;
+            const char* rp = ktile_next + row * kRowBytes;
+            const int z = swz(row);
+            floatx16 acc = {};
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                acc = mfma32(*reinterpret_cast<const half8*>(rp + (((2 * t + g) ^ z) << 4)), qb[t], acc);
+            sn.b[kb] = acc;
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+        }
+    }
+    if (HAS_NEXT) {
+        // Keep the probabilities in this phase: without these register
+        // fences the compiler sinks them past the mask branch into phase B,
+        // leaving the phase-A MFMAs with nothing to overlap.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[i]));
+        asm volatile("" : "+v"(lsum));
     }
     l_part += lsum;
+}
 
-    // O^T (head_dim x 32 queries) += V^T (head_dim x 64 keys) P^T.
-    const _Float16* vp = Vt + l32 * kVtStride + 8 * g;
+// Phase B.  MFMA: O^T += V^T P^T for the current tile (V^T operands by
+// transposed LDS reads).  VALU (when HAS_NEXT): the next tile's row maximum,
+// returned in log2 units (-inf if the tile has no visible key for the query).
+template <bool HAS_NEXT>
+__device__ __forceinline__ float phase_b(const char* __restrict__ vtile, const half8 (&pb)[4],
+                                         floatx16 (&oacc)[4], const TileScores& sn, float c2,
+                                         int l32, int g) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (ks >= 2 && !blk1) break;
-            const half8 a = *reinterpret_cast<const half8*>(vp + 32 * db * kVtStride + 16 * ks);
-            oacc[db] = mfma32(a, pb[ks], oacc[db]);
-        }
+        for (int db = 0; db < 4; ++db) oacc[db] = mfma32(load_vt(vtile, db, ks, l32, g), pb[ks], oacc[db]);
+    float mt = -INFINITY;
+    if (HAS_NEXT) {
+        float mx = fmaxf(sn.b[0][0], sn.b[1][0]);
+#pragma unroll
+        for (int i = 1; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sn.b[0][i]), sn.b[0][i + 1]);
+#pragma unroll
+        for (int i = 1; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sn.b[1][i]), sn.b[1][i + 1]);
+        mx = pair_max(mx);
+        mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 2, 0);
+    }
+    return mt;
+}
+
+// Raise the softmax reference when some query's tile maximum outgrew it by
+// more than tau; O and l are rescaled by 2^(m_old - m_new) in that case only.
+__device__ __forceinline__ void maybe_rescale(float mt, float& m_ref, float& l_part,
+                                              floatx16 (&oacc)[4]) {
+    if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau)) {
+        const float m_new = fmaxf(m_ref, mt);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        l_part *= alpha;
+        // In-place multiplies kept inside this rarely taken branch (the
+        // compiler would otherwise hoist them out with alpha = 1).
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                asm volatile("v_mul_f32 %0, %1, %0" : "+v"(oacc[db][i]) : "v"(alpha));
+        m_ref = m_new;
     }
 }
 
@@ -195,14 +317,17 @@ template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k, const _Float16* __restrict__ v,
     float* __restrict__ out, int seq_len, int n_q_heads, int n_kv_heads, int n_q_tiles, float c2,
-    int negate_q) {
-    __shared__ __attribute__((aligned(16))) _Float16 lds[kLdsBytes / 2];
-    _Float16* Ks = lds;
-    _Float16* Vt = lds + kKvTile * kKStride;
+    int q_mode) {
+    __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+    // K tile t lives in kbuf(t), V tile t in vbuf(t): two buffers each.
+    char* const kstage = lds;
+    char* const vstage = lds + kLdsKBytes;
+    auto kbuf = [&](int t) { return kstage + (t & 1) * kTileBytes; };
+    auto vbuf = [&](int t) { return vstage + (t & 1) * kTileBytes; };
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWaveSize - 1);
-    const int wave = tid / kWaveSize;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWaveSize);
     const int l32 = lane & 31;
     const int g = lane >> 5;
 
@@ -226,96 +351,81 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const int qw = q0 + wave * kQRowsPerWave;
     const int my_q = qw + l32;
 
+    const int kv_end = CAUSAL ? min(seq_len, q0 + kQTile) : seq_len;
+    const int n_tiles = (kv_end + kKvTile - 1) / kKvTile;
+
+    // Staging schedule: K tile t is copied two tiles ahead of its use in
+    // phase A, V tile t one tile ahead of its use in phase B.
+    stage_tile(k, n_kv_heads, hk, seq_len, 0, kbuf(0), wave, lane);
+    stage_tile(v, n_kv_heads, hk, seq_len, 0, vbuf(0), wave, lane);
+    if (n_tiles > 1) stage_tile(k, n_kv_heads, hk, seq_len, kKvTile, kbuf(1), wave, lane);
+
     // Q^T as the B operand: lane (l32, g) holds q[my_q][h][16t + 8g .. +8).
+    // q_mode 1 negates Q (negative scale), 2 zeroes it (scale 0).
     half8 qb[8];
     {
-        const bool in = my_q < seq_len;
+        const bool in = my_q < seq_len && q_mode != 2;
         const _Float16* qrow = q + ((size_t)my_q * n_q_heads + h) * kHeadDim + 8 * g;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
             qb[t] = in ? *reinterpret_cast<const half8*>(qrow + 16 * t) : half8{};
-        if (negate_q) {
+        if (q_mode == 1) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) qb[t] = -qb[t];
         }
     }
 
-    const int kv_end = CAUSAL ? min(seq_len, q0 + kQTile) : seq_len;
-    const int n_tiles = (kv_end + kKvTile - 1) / kKvTile;
-    int wave_tiles = n_tiles;
-    if (qw >= seq_len) {
-        wave_tiles = 0;  // every query of this wavefront is past the sequence end
-    } else if (CAUSAL) {
-        const int last = min(qw + kQRowsPerWave - 1, seq_len - 1);
-        wave_tiles = min(n_tiles, last / kKvTile + 1);
-    }
-
-    // Staging roles.  K: thread -> row kr (+16j), 16-byte chunk kc (coalesced
-    // 256-byte rows).  V: thread -> keys 4va..4va+3, head-dim chunk vc; the
-    // lanes of one 16-lane LDS write phase cover 16 distinct key groups.
-    const int kr = tid >> 4, kc = tid & 15;
-    const int va = tid & 15, vc = tid >> 4;
-    const int vpos = ((4 * va) & ~12) | ((va & 1) << 3) | (((va >> 1) & 1) << 2);
-    const size_t row_elems = (size_t)n_kv_heads * kHeadDim;
-    const _Float16* kbase = k + (size_t)hk * kHeadDim + kc * 8;
-    const _Float16* vbase = v + (size_t)hk * kHeadDim + vc * 8;
-
-    u32x4 kreg[4], vreg[4];
-    auto load_tile = [&](int kt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = kt + kr + 16 * j;
-            kreg[j] = row < seq_len ? *reinterpret_cast<const u32x4*>(kbase + (size_t)row * row_elems)
-                                    : u32x4{};
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = kt + 4 * va + r;
-            vreg[r] = row < seq_len ? *reinterpret_cast<const u32x4*>(vbase + (size_t)row * row_elems)
-                                    : u32x4{};
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<u32x4*>(Ks + (kr + 16 * j) * kKStride + kc * 8) = kreg[j];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int m = e >> 1;
-            uint32_t lo, hi;
-            if ((e & 1) == 0) {
-                lo = (vreg[0][m] & 0xffffu) | (vreg[1][m] << 16);
-                hi = (vreg[2][m] & 0xffffu) | (vreg[3][m] << 16);
-            } else {
-                lo = (vreg[0][m] >> 16) | (vreg[1][m] & 0xffff0000u);
-                hi = (vreg[2][m] >> 16) | (vreg[3][m] & 0xffff0000u);
-            }
-            *reinterpret_cast<u32x2*>(Vt + (8 * vc + e) * kVtStride + vpos) = u32x2{lo, hi};
-        }
-    };
-
     floatx16 oacc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) oacc[db] = floatx16{};
     float m_ref = -INFINITY, l_part = 0.0f;
+    half8 pb[4];
+    TileScores sa, sb;
 
-    load_tile(0);
-    for (int j = 0; j < n_tiles; ++j) {
-        const int kt = j * kKvTile;
-        if (j > 0) __syncthreads();  // every wavefront is done with the previous tile
-        store_tile();
+    // Prologue: scores and reference maximum of tile 0.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    {
+        phase_a<false, true>(kbuf(0), qb, sa, sa, pb, l_part, m_ref, c2, l32, g);
+        if (tile_needs_mask<CAUSAL>(0, qw, seq_len)) mask_scores<CAUSAL>(sa, 0, my_q, seq_len, g);
+        float mx = fmaxf(sa.b[0][0], sa.b[1][0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sa.b[0][i], sa.b[1][i]));
+        mx = pair_max(mx);
+        maybe_rescale((mx == -INFINITY) ? -INFINITY : mx * c2, m_ref, l_part, oacc);
+    }
+
+    // Pipeline step for tile j (its scores in sc), producing the scores of
+    // tile j + 1 in sn.  On entry K(j+1) and V(j) have been issued; the
+    // barrier also frees kbuf(j) and vbuf(j - 1) for K(j+2) and V(j+1).
+    auto step = [&](int j, TileScores& sc, TileScores& sn) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (j + 1 < n_tiles) load_tile(kt + kKvTile);  // in flight during this tile
-        if (j < wave_tiles) {
-            const bool masked =
-                (kt + kKvTile > seq_len) || (CAUSAL && kt + kKvTile - 1 > qw);
-            if (masked)
-                tile_step<true, CAUSAL>(Ks, Vt, qb, oacc, m_ref, l_part, kt, qw, my_q, seq_len, c2,
-                                        l32, g);
-            else
-                tile_step<false, CAUSAL>(Ks, Vt, qb, oacc, m_ref, l_part, kt, qw, my_q, seq_len, c2,
-                                         l32, g);
-        }
+        if (j + 2 < n_tiles) stage_tile(k, n_kv_heads, hk, seq_len, (j + 2) * kKvTile, kbuf(j + 2), wave, lane);
+        stage_tile(v, n_kv_heads, hk, seq_len, (j + 1) * kKvTile, vbuf(j + 1), wave, lane);
+        phase_a<true, true>(kbuf(j + 1), qb, sc, sn, pb, l_part, m_ref, c2, l32, g);
+        if (tile_needs_mask<CAUSAL>(j + 1, qw, seq_len)) mask_scores<CAUSAL>(sn, j + 1, my_q, seq_len, g);
+        const float mt = phase_b<true>(vbuf(j), pb, oacc, sn, c2, l32, g);
+        maybe_rescale(mt, m_ref, l_part, oacc);
+    };
+    // Last tile: probabilities and P.V only.
+    auto last = [&](int j, TileScores& sc) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        phase_a<true, false>(nullptr, qb, sc, sc, pb, l_part, m_ref, c2, l32, g);
+        phase_b<false>(vbuf(j), pb, oacc, sc, c2, l32, g);
+    };
+
+    int j = 0;
+    for (; j + 2 < n_tiles; j += 2) {
+        step(j, sa, sb);
+        step(j + 1, sb, sa);
+    }
+    if (j + 1 < n_tiles) {
+        step(j, sa, sb);
+        last(j + 1, sb);
+    } else {
+        last(j, sa);
     }
 
     // Epilogue: O / l, rows < seq_len only.  Lane (l32, g), register i of
@@ -380,15 +490,16 @@ extern "C" int fa_prefill(const void* q, const void* k, const void* v, float* ou
 
     // Base-2 softmax: fold log2(e) into the scale.  A negative scale is
     // applied as |scale| with Q negated (exact in f16), so the kernel's
-    // running maximum is always taken over a non-negative multiple of s.
-    const double c2d = std::fabs((double)scale) * 1.4426950408889634;
-    float c2 = (float)c2d;
-    int negate_q = scale < 0.0f ? 1 : 0;
+    // running maximum is always taken over a positive multiple of s.  A zero
+    // scale is applied as Q = 0 with multiplier 1 (every visible score 0),
+    // which keeps masked scores at -inf * 1 rather than -inf * 0.
+    int q_mode = scale < 0.0f ? 1 : (scale == 0.0f ? 2 : 0);
+    float c2 = q_mode == 2 ? 1.0f : (float)(std::fabs((double)scale) * 1.4426950408889634);
     const _Float16* qh = static_cast<const _Float16*>(q);
     const _Float16* kh = static_cast<const _Float16*>(k);
     const _Float16* vh = static_cast<const _Float16*>(v);
     int n_q_tiles = plan.n_q_tiles;
-    void* args[] = {&qh, &kh, &vh, &out, &seq_len, &n_q_heads, &n_kv_heads, &n_q_tiles, &c2, &negate_q};
+    void* args[] = {&qh, &kh, &vh, &out, &seq_len, &n_q_heads, &n_kv_heads, &n_q_tiles, &c2, &q_mode};
     const void* fn = causal ? reinterpret_cast<const void*>(&fa_prefill_kernel<true>)
                             : reinterpret_cast<const void*>(&fa_prefill_kernel<false>);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)plan.n_groups), dim3(kThreads), args, 0,

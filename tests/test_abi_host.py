@@ -89,9 +89,10 @@ def test_seq_len_zero_is_ok_without_gpu():
 def test_plan_geometry(S, nq, nkv, causal):
     p = fa.fa_prefill_plan(nq, nkv, S, 128, causal)
     # the LDS request is exactly the sum of the planes the kernel lays out
-    assert p.lds_bytes == p.lds_k_bytes + p.lds_vt_bytes
-    assert p.lds_k_bytes == p.kv_tile * (128 + 8) * 2
-    assert p.lds_vt_bytes == 128 * (p.kv_tile + 8) * 2
+    assert p.lds_bytes == p.lds_k_bytes + p.lds_v_bytes
+    assert p.lds_k_bytes == p.stages * p.kv_tile * 128 * 2
+    assert p.lds_v_bytes == p.stages * p.kv_tile * 128 * 2
+    assert p.lds_bytes <= 160 * 1024 // 2  # two work-groups fit one CU's 160 KiB
     assert p.threads_per_group == 64 * p.waves_per_group
     assert p.q_tile == 32 * p.waves_per_group
     assert p.n_q_tiles == math.ceil(S / p.q_tile)
