@@ -72,12 +72,14 @@ typedef struct fa_plan {
     int kv_tile;             /* key/value rows per LDS tile                       */
     int waves_per_group;     /* 64-lane wavefronts per work-group                 */
     int threads_per_group;   /* waves_per_group * 64                              */
+    int kv_splits;           /* wave groups per work-group, each taking a
+                                contiguous share of the query tile's KV tiles     */
     int n_q_tiles;           /* ceil(seq_len / q_tile)                            */
     long long n_groups;      /* work-groups launched: n_q_tiles * n_q_heads       */
-    int stages;              /* K/V tiles resident in LDS at once (buffering)     */
+    int stages;              /* K/V tiles resident in LDS per wave group          */
     int lds_bytes;           /* LDS per work-group: the sum of its planes         */
-    int lds_k_bytes;         /* K planes: stages x [kv_tile][head_dim] f16        */
-    int lds_v_bytes;         /* V planes: stages x [kv_tile][head_dim] f16        */
+    int lds_k_bytes;         /* K planes: kv_splits x stages x [kv_tile][head_dim] f16 */
+    int lds_v_bytes;         /* V planes: kv_splits x stages x [kv_tile][head_dim] f16 */
     long long kv_tiles_visited; /* KV tiles the grid visits (causal tiles skipped) */
 } fa_plan;
 

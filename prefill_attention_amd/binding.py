@@ -38,6 +38,7 @@ class FaPlan(ctypes.Structure):
         ("kv_tile", ctypes.c_int),
         ("waves_per_group", ctypes.c_int),
         ("threads_per_group", ctypes.c_int),
+        ("kv_splits", ctypes.c_int),
         ("n_q_tiles", ctypes.c_int),
         ("n_groups", ctypes.c_longlong),
         ("stages", ctypes.c_int),

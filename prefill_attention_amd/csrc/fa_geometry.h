@@ -17,6 +17,7 @@ constexpr int kThreads = kWaves * kWaveSize;
 constexpr int kQTile = kWaves * kQRowsPerWave;  // 128 query rows per work-group
 constexpr int kKvTile = 64;            // key/value rows per LDS tile
 constexpr int kStages = 2;             // LDS tiles in flight (double buffer)
+constexpr int kGroups = 1;             // wave groups splitting one query tile's KV range
 
 // LDS planes.  K and V tiles are both stored key-major with unpadded
 // 256-byte rows; the sixteen 16-byte chunks of a row are permuted by

@@ -67,6 +67,7 @@ int make_plan(int n_q_heads, int n_kv_heads, int seq_len, int head_dim, int caus
         plan->kv_tile = kKvTile;
         plan->waves_per_group = kWaves;
         plan->threads_per_group = kThreads;
+        plan->kv_splits = kGroups;
         plan->n_q_tiles = (int)n_q_tiles;
         plan->n_groups = n_groups;
         plan->stages = kStages;

@@ -300,15 +300,15 @@ __device__ __forceinline__ void maybe_rescale(float mt, float& m_ref, float& l_p
                                               floatx16 (&oacc)[4]) {
     if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau)) {
         const float m_new = fmaxf(m_ref, mt);
+        // A side effect keeps this rarely taken block from being speculated
+        // (the compiler would otherwise multiply by alpha = 1 on every tile).
+        // The multiplies themselves stay ordinary code: they read MFMA
+        // results, and only visible code gets the MFMA-to-VALU wait states.
+        asm volatile("" ::: "memory");
         const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
         l_part *= alpha;
-        // In-place multiplies kept inside this rarely taken branch (the
-        // compiler would otherwise hoist them out with alpha = 1).
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                asm volatile("v_mul_f32 %0, %1, %0" : "+v"(oacc[db][i]) : "v"(alpha));
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
         m_ref = m_new;
     }
 }

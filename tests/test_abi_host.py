@@ -90,11 +90,11 @@ def test_plan_geometry(S, nq, nkv, causal):
     p = fa.fa_prefill_plan(nq, nkv, S, 128, causal)
     # the LDS request is exactly the sum of the planes the kernel lays out
     assert p.lds_bytes == p.lds_k_bytes + p.lds_v_bytes
-    assert p.lds_k_bytes == p.stages * p.kv_tile * 128 * 2
-    assert p.lds_v_bytes == p.stages * p.kv_tile * 128 * 2
-    assert p.lds_bytes <= 160 * 1024 // 2  # two work-groups fit one CU's 160 KiB
+    assert p.lds_k_bytes == p.kv_splits * p.stages * p.kv_tile * 128 * 2
+    assert p.lds_v_bytes == p.kv_splits * p.stages * p.kv_tile * 128 * 2
+    assert p.lds_bytes * (8 // p.waves_per_group) <= 160 * 1024  # 8 resident waves per CU fit 160 KiB
     assert p.threads_per_group == 64 * p.waves_per_group
-    assert p.q_tile == 32 * p.waves_per_group
+    assert p.q_tile * p.kv_splits == 32 * p.waves_per_group
     assert p.n_q_tiles == math.ceil(S / p.q_tile)
     assert p.n_groups == p.n_q_tiles * nq
     # KV tiles visited: causal groups stop at their last query row

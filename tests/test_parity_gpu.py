@@ -87,6 +87,16 @@ def test_tail_sweep_causal(fa, S, heads):
     assert within_tolerance(err), (S, heads, err)
 
 
+@pytest.mark.parametrize("S", [300, 700, 1024, 1500])
+def test_peaked_rows_rescale(fa, S):
+    """K x 3 makes the row maximum grow mid-sequence, so the running softmax
+    reference is raised and O rescaled on many tiles (the rescale multiplies
+    read MFMA results; a missing MFMA-to-VALU wait shows up here)."""
+    q, k, v = make_custom_inputs(S, 4, 1, seed=4000 + S, k_mult=3.0)
+    err = parity_errors(_run(fa, q, k, v), attention_f64(q, k, v, SCALE, True))
+    assert within_tolerance(err), (S, err)
+
+
 @pytest.mark.parametrize("S", [1, 17, 64, 65, 200, 256])
 def test_non_causal(fa, S):
     q, k, v = make_custom_inputs(S, 4, 2, seed=2000 + S)
