@@ -145,18 +145,26 @@ __device__ __forceinline__ void stage_tile(const _Float16* __restrict__ src, int
 // A operand of O^T += V^T P^T for head-dim block db and key step ks: the
 // 32 x 16 slice V^T[32db .. 32db+31][16ks .. 16ks+15] in the slot order of
 // the probability registers (slot (g, e) <-> key 16ks + 8(e/4) + 4g + e%4).
-// Two transposed reads: within each 16-lane group, lane i addresses row
-// i/4, head-dim columns 4(i%4) .. +3 of the group's 16 columns, and receives
-// column i of the four rows.
-__device__ __forceinline__ half8 load_vt(const char* vtile, int db, int ks, int l32, int g) {
+// Two transposed reads (h = 0, 1): within each 16-lane group, lane i = 4r +
+// qd addresses key 16ks + 8h + 4g + r, head-dim columns 4(i%4) .. +3 of the
+// group's 16 columns, and receives column i of the four keys.
+//
+// The key's swizzle, 4r + 2h + g, does not depend on ks, so the byte offset
+// splits into a per-lane part for each (db, h) -- vt_lane_offset, computed
+// once -- and 4096 ks, which the LDS instruction takes as an immediate.
+__device__ __forceinline__ int vt_lane_offset(int db, int h, int l32, int g) {
     const int i = l32 & 15;
     const int r = i >> 2, qd = i & 3;
     const int chunk = 4 * db + 2 * (l32 >> 4) + (qd >> 1);
+    const int key = 8 * h + 4 * g + r;
+    return key * kRowBytes + ((chunk ^ swz(key)) << 4) + ((qd & 1) << 3);
+}
+
+__device__ __forceinline__ half8 load_vt(const char* vtile, const int (&vt_off)[8], int db, int ks) {
     half8 a;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int key = 16 * ks + 8 * h + 4 * g + r;
-        const char* p = vtile + key * kRowBytes + ((chunk ^ swz(key)) << 4) + ((qd & 1) << 3);
+        const char* p = vtile + 16 * ks * kRowBytes + vt_off[2 * db + h];
         const short4v t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
         const half4 hv = __builtin_bit_cast(half4, t);
         a[4 * h + 0] = hv[0];
@@ -166,11 +174,6 @@ __device__ __forceinline__ half8 load_vt(const char* vtile, int db, int ks, int 
     }
     return a;
 }
-
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002;
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
 
 // Scores of one 64-key tile for this wavefront's 32 queries: S^T blocks for
 // keys [0, 32) and [32, 64) of the tile.
@@ -198,98 +201,102 @@ __device__ __forceinline__ bool tile_needs_mask(int t, int qw, int seq_len) {
            (CAUSAL && t * kKvTile + kKvTile - 1 > qw);
 }
 
-// Phase A of the tile pipeline.  VALU (when HAS_CUR): probabilities of the current tile,
-// p = 2^(s*c2 - m) rounded to f16 (the B operand of O^T += V^T P^T), and
-// their row sum.  MFMA (when HAS_NEXT): scores of the next tile, S^T = K Q^T,
-// with K read from LDS.  The two streams are independent, so they are
-// interleaved: one MFMA, one LDS read for a later MFMA, six VALU ops.
-template <bool HAS_CUR, bool HAS_NEXT>
+// Phase A of the tile pipeline, as 16 explicit issue slots.  Slot i
+// (kb = i / 8, t = i % 8):
+//   MFMA (when HAS_NEXT): S^T block kb of the next tile += K fragment t x Q^T
+//     fragment t; the K fragment was read from LDS four slots earlier into
+//     one of four rotating registers, and the read for slot i + 4 is issued
+//     right after;
+//   VALU (when HAS_CUR): two probabilities of the current tile, p = 2^(s*c2
+//     - m) rounded to f16 into the B operands of O^T += V^T P^T, and their
+//     contribution to the row sum.
+// With PREFETCH_V the last four slots also read phase B's first four V^T
+// fragments.  Hard scheduling barriers between slots keep every K read four
+// MFMAs ahead of its use and the exponentials spread under the MFMAs.
+template <bool HAS_CUR, bool HAS_NEXT, bool PREFETCH_V>
 __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next, const half8 (&qb)[8],
                                         const TileScores& sc, TileScores& sn, half8 (&pb)[4],
-                                        float& l_part, float m_ref, float c2, int l32, int g) {
+                                        float& l_part, float m_ref, float c2, int l32, int g,
+                                        const char* __restrict__ vtile, const int (&vt_off)[8],
+                                        half8 (&vf)[4]) {
     float lsum = 0.0f;
     const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int kb = 0; kb < 2 && HAS_CUR; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc.b[kb][i], c2, -m_ref));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc.b[kb][i + 1], c2, -m_ref));
-            const floatx2 pf = {p0, p1};
-            const half2v ph = __builtin_convertvector(pf, half2v);
-            pb[2 * kb + (i >> 3)][i & 7] = ph[0];
-            pb[2 * kb + (i >> 3)][(i & 7) + 1] = ph[1];
-            lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
-        }
+    // K fragment (kb, t): key row 32kb + l32, head-dim 16t + 8g.
+    const int z = swz(l32);  // swz(32kb + l32) == swz(l32)
+    const char* rp = ktile_next + l32 * kRowBytes;
+    auto kread = [&](int i) {
+        const int kb = i >> 3, t = i & 7;
+        return *reinterpret_cast<const half8*>(rp + kb * 32 * kRowBytes + (((2 * t + g) ^ z) << 4));
+    };
+    // VALU chunk c: probabilities 2c and 2c + 1 of the current tile.
+    auto valu_chunk = [&](int c) {
+        const int kb = c >> 3, e = 2 * (c & 7);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc.b[kb][e], c2, -m_ref));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc.b[kb][e + 1], c2, -m_ref));
+        const floatx2 pf = {p0, p1};
+        const half2v ph = __builtin_convertvector(pf, half2v);
+        pb[2 * kb + (e >> 3)][e & 7] = ph[0];
+        pb[2 * kb + (e >> 3)][(e & 7) + 1] = ph[1];
+        lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
+    };
+    half8 kf[4];
+    floatx16 acc[2] = {};
     if (HAS_NEXT) {
-        // K fragment t of block kb: key row 32kb + l32, head-dim 16t + 8g.
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int row = 32 * kb + l32;
-            const char* rp = ktile_next + row * kRowBytes;
-            const int z = swz(row);
-            floatx16 acc = {};
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                acc = mfma32(*reinterpret_cast<const half8*>(rp + (((2 * t + g) ^ z) << 4)), qb[t], acc);
-            sn.b[kb] = acc;
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
-#pragma unroll
-        for (int i = 0; i < 12; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
-        }
+        for (int i = 0; i < 4; ++i) kf[i] = kread(i);
     }
-    if (HAS_NEXT) {
-        // Keep the probabilities in this phase: without these register
-        // fences the compiler sinks them past the mask branch into phase B,
-        // leaving the phase-A MFMAs with nothing to overlap.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (HAS_NEXT) {
+            acc[i >> 3] = mfma32(kf[i & 3], qb[i & 7], acc[i >> 3]);
+            if (i + 4 < 16) kf[i & 3] = kread(i + 4);
+        }
+        // The first four V^T fragments of phase B, read while the K reads wind down.
+        if (PREFETCH_V && i >= 12) vf[i - 12] = load_vt(vtile, vt_off, i - 12, 0);
+        if (HAS_CUR) valu_chunk(i);
+    }
+    if (HAS_CUR && HAS_NEXT) {
+        // Register fences: keep the probabilities in this phase (code
+        // motion before scheduling would otherwise sink them into phase B).
 #pragma unroll
         for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[i]));
         asm volatile("" : "+v"(lsum));
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (HAS_NEXT) {
+        sn.b[0] = acc[0];
+        sn.b[1] = acc[1];
+    }
     l_part += lsum;
 }
 
-// Phase B.  MFMA: O^T += V^T P^T for the current tile (V^T operands by
-// transposed LDS reads).  VALU (when HAS_NEXT): the next tile's row maximum,
-// returned in log2 units (-inf if the tile has no visible key for the query).
+// Phase B, as 16 explicit issue slots.  Slot f (ks = f / 4, db = f % 4):
+// MFMA O^T block db += V^T fragment (db, ks) x P^T fragment ks, the V^T
+// fragment (two transposed LDS reads) having been read four slots earlier
+// (the first four in phase A), then the read for slot f + 4.  VALU (when
+// HAS_NEXT): the next tile's row maximum, returned in log2 units (-inf if the
+// tile has no visible key for the query), spread over the slots.
 template <bool HAS_NEXT>
 __device__ __forceinline__ float phase_b(const char* __restrict__ vtile, const half8 (&pb)[4],
                                          floatx16 (&oacc)[4], const TileScores& sn, float c2,
-                                         int l32, int g) {
+                                         int l32, int g, const int (&vt_off)[8], half8 (&vf)[4]) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[db] = mfma32(load_vt(vtile, db, ks, l32, g), pb[ks], oacc[db]);
+    for (int f = 0; f < 16; ++f) {
+        __builtin_amdgcn_sched_barrier(0);
+        oacc[f & 3] = mfma32(vf[f & 3], pb[f >> 2], oacc[f & 3]);
+        if (f + 4 < 16) vf[f & 3] = load_vt(vtile, vt_off, (f + 4) & 3, (f + 4) >> 2);
+        if (HAS_NEXT) {
+            const int kb = f >> 3, i = 2 * (f & 7);
+            mx = fmaxf(fmaxf(mx, sn.b[kb][i]), sn.b[kb][i + 1]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float mt = -INFINITY;
     if (HAS_NEXT) {
-        float mx = fmaxf(sn.b[0][0], sn.b[1][0]);
-#pragma unroll
-        for (int i = 1; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sn.b[0][i]), sn.b[0][i + 1]);
-#pragma unroll
-        for (int i = 1; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sn.b[1][i]), sn.b[1][i + 1]);
         mx = pair_max(mx);
         mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 2, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 2, 0);
     }
     return mt;
 }
@@ -375,6 +382,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
         }
     }
 
+    int vt_off[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vt_off[i] = vt_lane_offset(i >> 1, i & 1, l32, g);
+
     floatx16 oacc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) oacc[db] = floatx16{};
@@ -386,7 +397,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     {
-        phase_a<false, true>(kbuf(0), qb, sa, sa, pb, l_part, m_ref, c2, l32, g);
+        half8 vf_unused[4];
+        phase_a<false, true, false>(kbuf(0), qb, sa, sa, pb, l_part, m_ref, c2, l32, g, nullptr, vt_off, vf_unused);
         if (tile_needs_mask<CAUSAL>(0, qw, seq_len)) mask_scores<CAUSAL>(sa, 0, my_q, seq_len, g);
         float mx = fmaxf(sa.b[0][0], sa.b[1][0]);
 #pragma unroll
@@ -403,17 +415,19 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
         __syncthreads();
         if (j + 2 < n_tiles) stage_tile(k, n_kv_heads, hk, seq_len, (j + 2) * kKvTile, kbuf(j + 2), wave, lane);
         stage_tile(v, n_kv_heads, hk, seq_len, (j + 1) * kKvTile, vbuf(j + 1), wave, lane);
-        phase_a<true, true>(kbuf(j + 1), qb, sc, sn, pb, l_part, m_ref, c2, l32, g);
+        half8 vf[4];
+        phase_a<true, true, true>(kbuf(j + 1), qb, sc, sn, pb, l_part, m_ref, c2, l32, g, vbuf(j), vt_off, vf);
         if (tile_needs_mask<CAUSAL>(j + 1, qw, seq_len)) mask_scores<CAUSAL>(sn, j + 1, my_q, seq_len, g);
-        const float mt = phase_b<true>(vbuf(j), pb, oacc, sn, c2, l32, g);
+        const float mt = phase_b<true>(vbuf(j), pb, oacc, sn, c2, l32, g, vt_off, vf);
         maybe_rescale(mt, m_ref, l_part, oacc);
     };
     // Last tile: probabilities and P.V only.
     auto last = [&](int j, TileScores& sc) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        phase_a<true, false>(nullptr, qb, sc, sc, pb, l_part, m_ref, c2, l32, g);
-        phase_b<false>(vbuf(j), pb, oacc, sc, c2, l32, g);
+        half8 vf[4];
+        phase_a<true, false, true>(nullptr, qb, sc, sc, pb, l_part, m_ref, c2, l32, g, vbuf(j), vt_off, vf);
+        phase_b<false>(vbuf(j), pb, oacc, sc, c2, l32, g, vt_off, vf);
     };
 
     int j = 0;
