@@ -11,7 +11,9 @@ arithmetic).
 """
 
 from .attention import (
+    attention_chunk_f64,
     attention_f64,
+    query_positions,
     kv_head_for,
     scores_f64,
     visible_mask,
@@ -21,7 +23,9 @@ from .attention import (
 from .compare import ATOL, RTOL, REL_FLOOR, parity_errors, within_tolerance
 
 __all__ = [
+    "attention_chunk_f64",
     "attention_f64",
+    "query_positions",
     "kv_head_for",
     "scores_f64",
     "visible_mask",

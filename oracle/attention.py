@@ -28,7 +28,9 @@ sequence is visible.
 
 Readings where the pages are silent (each listed in the design doc):
 * grouped-query mapping: consecutive groups, hk = h // (n_q_heads // n_kv_heads);
-* query positions equal key positions 0..S-1 (no earlier KV cache);
+* a full prefill's query positions equal key positions 0..S-1; a chunk of Q
+  new tokens over a cache of S - Q tokens has queries at S - Q .. S - 1
+  (``query_positions``);
 * ``scale`` multiplies the raw dot product; the value used is the float32
   value the GPU receives, widened to float64;
 * inputs are the exact f16 values, widened to float64.
@@ -99,6 +101,53 @@ def combine_values(p: np.ndarray, v_h: np.ndarray) -> np.ndarray:
     return p @ v_h
 
 
+def query_positions(q_len: int, kv_len: int) -> np.ndarray:
+    """Sequence positions of the q_len queries of a chunk over kv_len keys.
+
+    The pages' kernel compares each key index with the query's position in a
+    position-indexed KV cache (valid = key <= query position and key below
+    the stored-KV end: "28 · r23", §3.2), and the K/V producer writes each
+    new token's K/V at that token's position ("11 · P5 — prefill gap
+    session", §3.2, the store_kv_f16 kernel).  For q_len new tokens appended
+    to a cache holding kv_len - q_len tokens, query row i therefore sits at
+    position kv_len - q_len + i.  A full prefill is q_len == kv_len.
+    """
+    if not 0 <= q_len <= kv_len:
+        raise ValueError("need 0 <= q_len <= kv_len")
+    return np.arange(kv_len - q_len, kv_len, dtype=np.int64)
+
+
+def _attention(qf, kf, vf, scale64, causal, row_idx, positions, return_probs):
+    """Per-head plain softmax attention of the query rows ``row_idx`` (at
+    sequence ``positions``) over every key of kf/vf."""
+    n_q, hd = qf.shape[1], qf.shape[2]
+    S, n_kv = kf.shape[0], kf.shape[1]
+    visible = visible_mask(positions, S, causal)
+    out = np.empty((row_idx.shape[0], n_q, hd), dtype=np.float64)
+    probs = np.empty((n_q, row_idx.shape[0], S), dtype=np.float64) if return_probs else None
+    for h in range(n_q):
+        hk = kv_head_for(h, n_q, n_kv)
+        s = scores_f64(qf[row_idx, h, :], kf[:, hk, :], scale64)
+        p = softmax_rows(s, visible)
+        out[:, h, :] = combine_values(p, vf[:, hk, :])
+        if return_probs:
+            probs[h] = p
+    if return_probs:
+        return out, probs
+    return out
+
+
+def _checked(q, k, v):
+    qf, kf, vf = _as_f64(q), _as_f64(k), _as_f64(v)
+    if qf.ndim != 3 or kf.ndim != 3 or vf.ndim != 3:
+        raise ValueError("q, k, v must be [tokens, heads, hd]")
+    if kf.shape != vf.shape or kf.shape[2] != qf.shape[2]:
+        raise ValueError("k and v must be [S, n_kv_heads, hd] with q's hd")
+    if not (np.all(np.isfinite(qf)) and np.all(np.isfinite(kf)) and np.all(np.isfinite(vf))):
+        raise ValueError("non-finite inputs are outside the contract")
+    return qf, kf, vf
+
+
 def attention_f64(
     q,
     k,
@@ -118,31 +167,29 @@ def attention_f64(
     Returns o [len(rows) or S, n_q_heads, hd] float64, and with
     ``return_probs`` also p [n_q_heads, R, S].
     """
-    qf, kf, vf = _as_f64(q), _as_f64(k), _as_f64(v)
-    if qf.ndim != 3 or kf.ndim != 3 or vf.ndim != 3:
-        raise ValueError("q, k, v must be [S, heads, hd]")
-    S, n_q, hd = qf.shape
-    if kf.shape != vf.shape or kf.shape[0] != S or kf.shape[2] != hd:
-        raise ValueError("k and v must be [S, n_kv_heads, hd] matching q")
-    n_kv = kf.shape[1]
-    if not (np.all(np.isfinite(qf)) and np.all(np.isfinite(kf)) and np.all(np.isfinite(vf))):
-        raise ValueError("non-finite inputs are outside the contract")
+    qf, kf, vf = _checked(q, k, v)
+    S = qf.shape[0]
+    if kf.shape[0] != S:
+        raise ValueError("k and v must have q's sequence length")
     scale64 = float(np.float32(scale))
     row_idx = np.arange(S, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
-    visible = visible_mask(row_idx, S, causal)
+    return _attention(qf, kf, vf, scale64, causal, row_idx, row_idx, return_probs)
 
-    out = np.empty((row_idx.shape[0], n_q, hd), dtype=np.float64)
-    probs = np.empty((n_q, row_idx.shape[0], S), dtype=np.float64) if return_probs else None
-    for h in range(n_q):
-        hk = kv_head_for(h, n_q, n_kv)
-        s = scores_f64(qf[row_idx, h, :], kf[:, hk, :], scale64)
-        p = softmax_rows(s, visible)
-        out[:, h, :] = combine_values(p, vf[:, hk, :])
-        if return_probs:
-            probs[h] = p
-    if return_probs:
-        return out, probs
-    return out
+
+def attention_chunk_f64(q, k, v, scale: float, causal: bool = True, rows=None):
+    """Chunked prefill: q_len new queries attending over a kv_len-token KV cache.
+
+    q: [q_len, n_q_heads, hd]; k, v: [kv_len, n_kv_heads, hd], q_len <= kv_len,
+    the chunk's own K/V being the last q_len rows.  Query row i is at position
+    ``query_positions(q_len, kv_len)[i]``; otherwise the arithmetic is
+    ``attention_f64``'s.  ``rows`` restricts the computation to a subset of
+    query rows (indices into q).  Returns o [len(rows) or q_len, n_q_heads, hd].
+    """
+    qf, kf, vf = _checked(q, k, v)
+    positions = query_positions(qf.shape[0], kf.shape[0])
+    row_idx = np.arange(qf.shape[0], dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    scale64 = float(np.float32(scale))
+    return _attention(qf, kf, vf, scale64, causal, row_idx, positions[row_idx], False)
 
 
 def attention_rows_blocked(q, k, v, scale: float, causal: bool = True, rows=None, block: int = 512):

@@ -12,10 +12,13 @@ no activation statistics, so N(0, 1) draws rounded to f16 stand in for the
 projected Q/K/V activations at those shapes.
 
 Recipe (per workload, from one CPU generator seeded with ``seed``):
-    q = f16(randn([S, n_q_heads, 128]))
+    q = f16(randn([Q, n_q_heads, 128]))
     k = f16(k_mult * randn([S, n_kv_heads, 128]))     (k_mult = 3 for the GQA case)
     v = f16(randn([S, n_kv_heads, 128]))
-drawn in that order.  scale = float32(1 / sqrt(128)).
+drawn in that order, S = ``seq_len`` keys and Q = ``q_len`` queries.  A
+full prefill has Q = S.  A chunked prefill (Q < S) is the last Q tokens of
+an S-token sequence whose first S - Q tokens are already in the KV cache: its
+queries sit at positions S - Q .. S - 1.  scale = float32(1 / sqrt(128)).
 """
 
 from __future__ import annotations
@@ -43,11 +46,22 @@ class Workload:
     head_dim: int = HEAD_DIM
     # number of query rows per head the oracle checks (None: all rows)
     oracle_rows: int | None = None
+    # queries (the last q_len positions of the sequence); None: a full prefill
+    q_rows: int | None = None
+
+    @property
+    def q_len(self) -> int:
+        return self.seq_len if self.q_rows is None else self.q_rows
+
+    @property
+    def chunked(self) -> bool:
+        return self.q_len != self.seq_len
 
     @property
     def visible_pairs(self) -> int:
-        S = self.seq_len
-        return S * (S + 1) // 2 if self.causal else S * S
+        S, Q = self.seq_len, self.q_len
+        off = S - Q
+        return Q * off + Q * (Q + 1) // 2 if self.causal else Q * S
 
     @property
     def flop(self) -> int:
@@ -55,7 +69,7 @@ class Workload:
         return 4 * self.head_dim * self.n_q_heads * self.visible_pairs
 
     def describe(self) -> dict:
-        return {
+        d = {
             "workload": self.name,
             "n_q_heads": self.n_q_heads,
             "n_kv_heads": self.n_kv_heads,
@@ -65,6 +79,10 @@ class Workload:
             "dtype_in": "f16",
             "dtype_out": "f32",
         }
+        if self.chunked:
+            d["q_len"] = self.q_len
+            d["kv_len"] = self.seq_len
+        return d
 
 
 WORKLOADS = {
@@ -80,6 +98,10 @@ WORKLOADS = {
         "long_16k", "long GQA causal prefill, 32 q / 8 kv heads, S=16384, hd=128", 32, 8, 16384, seed=5,
         oracle_rows=256,
     ),
+    "chunk_512_4k": Workload(
+        "chunk_512_4k", "7B-layer chunked causal prefill: 512 new tokens over a 3584-token KV cache, "
+        "32/32 heads, hd=128", 32, 32, 4096, seed=6, q_rows=512,
+    ),
 }
 
 # Workload the throughput figure is quoted on.
@@ -87,10 +109,11 @@ HEADLINE = "7b_2659"
 
 
 def make_inputs(wl: Workload, seed: int | None = None, device: str = "cpu"):
-    """(q, k, v) f16 tensors [S, heads, hd] drawn as described in the module docstring."""
+    """(q, k, v) f16 tensors: q [q_len, n_q_heads, hd], k/v [seq_len, n_kv_heads, hd],
+    drawn as described in the module docstring."""
     g = torch.Generator(device="cpu").manual_seed(wl.seed if seed is None else seed)
     S, hd = wl.seq_len, wl.head_dim
-    q = torch.randn([S, wl.n_q_heads, hd], dtype=torch.float32, generator=g).half()
+    q = torch.randn([wl.q_len, wl.n_q_heads, hd], dtype=torch.float32, generator=g).half()
     k = (wl.k_mult * torch.randn([S, wl.n_kv_heads, hd], dtype=torch.float32, generator=g)).half()
     v = torch.randn([S, wl.n_kv_heads, hd], dtype=torch.float32, generator=g).half()
     if device != "cpu":
@@ -99,9 +122,11 @@ def make_inputs(wl: Workload, seed: int | None = None, device: str = "cpu"):
 
 
 def make_custom_inputs(seq_len: int, n_q_heads: int, n_kv_heads: int, seed: int,
-                       head_dim: int = HEAD_DIM, k_mult: float = 1.0):
-    """Same recipe at an arbitrary shape (tail sweeps, edge cases)."""
-    wl = Workload("custom", "custom", n_q_heads, n_kv_heads, seq_len, seed, k_mult=k_mult, head_dim=head_dim)
+                       head_dim: int = HEAD_DIM, k_mult: float = 1.0, q_len: int | None = None):
+    """Same recipe at an arbitrary shape (tail sweeps, edge cases); ``q_len``
+    queries at the last positions of a ``seq_len``-token sequence (default all)."""
+    wl = Workload("custom", "custom", n_q_heads, n_kv_heads, seq_len, seed, k_mult=k_mult, head_dim=head_dim,
+                  q_rows=q_len)
     return make_inputs(wl)
 
 

@@ -25,7 +25,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle.attention as oa
-from oracle import attention_f64, parity_errors, within_tolerance
+from oracle import attention_chunk_f64, attention_f64, parity_errors, within_tolerance
 from oracle.attention import attention_rows_blocked
 from prefill_attention_amd.workloads import SCALE, WORKLOADS, make_custom_inputs, make_inputs, row_subset
 
@@ -212,7 +212,81 @@ def pin_invariants():
     return fails
 
 
-PINS = {"golden": pin_golden, "library": pin_library, "brute": pin_brute, "invariants": pin_invariants}
+def brute_force_positions(q, k, v, scale, causal, first_pos):
+    """Scalar loops; query row i at sequence position first_pos + i."""
+    qn, kn, vn = (np.asarray(t, dtype=np.float64).tolist() for t in (q, k, v))
+    Q, n_q, hd = len(qn), len(qn[0]), len(qn[0][0])
+    S, n_kv = len(kn), len(kn[0])
+    group = n_q // n_kv
+    scale = float(np.float32(scale))
+    out = [[[0.0] * hd for _ in range(n_q)] for _ in range(Q)]
+    for h in range(n_q):
+        hk = h // group
+        for i in range(Q):
+            keys = range(first_pos + i + 1) if causal else range(S)
+            s = [scale * math.fsum(qn[i][h][d] * kn[j][hk][d] for d in range(hd)) for j in keys]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            total = math.fsum(w)
+            for d in range(hd):
+                out[i][h][d] = math.fsum(wj * vn[j][hk][d] for wj, j in zip(w, keys)) / total
+    return np.asarray(out)
+
+
+def pin_chunk():
+    """Chunked prefill (queries at the last q_len of kv_len positions)."""
+    fails = []
+
+    def check(name, cond):
+        if not cond:
+            fails.append(name)
+
+    try:
+        # library: torch SDPA float64 with the boolean mask written out here
+        for (Q, S, nq, nkv, seed) in ((37, 100, 4, 2, 31), (1, 64, 2, 1, 32), (64, 64, 2, 2, 33)):
+            q, k, v = make_custom_inputs(S, nq, nkv, seed=seed, q_len=Q)
+            qt = torch.as_tensor(_f(q)).permute(1, 0, 2)[None]
+            kt = torch.as_tensor(_f(k)).permute(1, 0, 2)[None].repeat_interleave(nq // nkv, dim=1)
+            vt = torch.as_tensor(_f(v)).permute(1, 0, 2)[None].repeat_interleave(nq // nkv, dim=1)
+            mask = torch.tensor([[j <= S - Q + i for j in range(S)] for i in range(Q)])
+            for causal in (True, False):
+                ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask if causal else None,
+                                                     scale=float(np.float32(SCALE)))[0].permute(1, 0, 2).numpy()
+                got = attention_chunk_f64(q, k, v, SCALE, causal)
+                check(f"sdpa Q={Q} S={S} causal={causal}",
+                      got.shape == ref.shape and np.max(np.abs(got - ref)) <= 1e-12)
+        # the chunk is the last rows of the full-sequence attention whose
+        # earlier queries are anything (here: another seeded draw)
+        Q, S = 23, 90
+        q, k, v = make_custom_inputs(S, 4, 2, seed=34, q_len=Q)
+        q_prefix, _, _ = make_custom_inputs(S, 4, 2, seed=35, q_len=S - Q)
+        q_full = torch.cat([q_prefix, q], dim=0)
+        for causal in (True, False):
+            full = attention_f64(q_full, k, v, SCALE, causal)[S - Q:]
+            got = attention_chunk_f64(q, k, v, SCALE, causal)
+            # (same arithmetic; a BLAS call over more rows may round differently)
+            check(f"last rows of full causal={causal}", np.max(np.abs(got - full)) <= 1e-12)
+        # brute force with explicit positions
+        for (Q, S, seed) in ((3, 7, 36), (1, 5, 37), (6, 6, 38)):
+            q, k, v = make_custom_inputs(S, 2, 1, seed=seed, head_dim=4, k_mult=2.0, q_len=Q)
+            for causal in (True, False):
+                ref = brute_force_positions(_f(q), _f(k), _f(v), 0.7, causal, S - Q)
+                got = attention_chunk_f64(q, k, v, 0.7, causal)
+                check(f"brute Q={Q} S={S} causal={causal}", np.max(np.abs(got - ref)) <= 1e-12)
+        # special cases: q_len == kv_len is the full prefill; one query sees every key
+        q, k, v = make_custom_inputs(50, 2, 2, seed=39)
+        check("q_len == kv_len", np.array_equal(attention_chunk_f64(q, k, v, SCALE, True),
+                                                attention_f64(q, k, v, SCALE, True)))
+        q1, k1, v1 = make_custom_inputs(50, 2, 2, seed=40, q_len=1)
+        check("single query sees all keys", np.array_equal(attention_chunk_f64(q1, k1, v1, SCALE, True),
+                                                           attention_chunk_f64(q1, k1, v1, SCALE, False)))
+    except Exception as e:
+        fails.append(f"raised {e!r}")
+    return fails
+
+
+PINS = {"golden": pin_golden, "library": pin_library, "brute": pin_brute, "invariants": pin_invariants,
+        "chunk": pin_chunk}
 
 
 # --------------------------------------------------------------------- tests
@@ -315,6 +389,14 @@ def _mut_gqa_modulo(h, nq, nkv):
     return h % nkv
 
 
+def _mut_positions_from_zero(q_len, kv_len):
+    return np.arange(q_len, dtype=np.int64)
+
+
+def _mut_positions_off_by_one(q_len, kv_len):
+    return np.arange(kv_len - q_len + 1, kv_len + 1, dtype=np.int64)
+
+
 def _mut_combine_unmasked_mean(p, v_h):
     return np.broadcast_to(v_h.mean(axis=0), (p.shape[0], v_h.shape[1])).copy()
 
@@ -331,6 +413,8 @@ MUTANTS = {
     "softmax sign flipped": ("softmax_rows", _mut_softmax_sign),
     "GQA modulo mapping": ("kv_head_for", _mut_gqa_modulo),
     "values ignore p": ("combine_values", _mut_combine_unmasked_mean),
+    "chunk positions from 0": ("query_positions", _mut_positions_from_zero),
+    "chunk positions off by one": ("query_positions", _mut_positions_off_by_one),
 }
 
 
