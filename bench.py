@@ -59,7 +59,7 @@ def measured_traffic(workload_key: str):
 def cpu_baseline(wl, q, k, v, gpu_out, scale, budget_s: float = 12.0) -> dict:
     """Time the float64 oracle on whole heads of the workload, about budget_s of CPU work."""
     import numpy as np
-    from oracle import attention_f64, parity_errors
+    from oracle import attention_chunk_f64, attention_f64, parity_errors
 
     try:
         import threadpoolctl
@@ -75,7 +75,8 @@ def cpu_baseline(wl, q, k, v, gpu_out, scale, budget_s: float = 12.0) -> dict:
         h = heads
         hk = h // group
         t0 = time.perf_counter()
-        ref = attention_f64(q[:, h:h + 1], k[:, hk:hk + 1], v[:, hk:hk + 1], scale, wl.causal)
+        oracle_fn = attention_chunk_f64 if wl.chunked else attention_f64
+        ref = oracle_fn(q[:, h:h + 1], k[:, hk:hk + 1], v[:, hk:hk + 1], scale, wl.causal)
         t_used += time.perf_counter() - t0
         worst = max(worst, parity_errors(gpu_np[:, h:h + 1], ref)["max_abs"])
         heads += 1
@@ -85,7 +86,7 @@ def cpu_baseline(wl, q, k, v, gpu_out, scale, budget_s: float = 12.0) -> dict:
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"first {heads} of {wl.n_q_heads} query heads, all {wl.seq_len} rows "
+        "sample": f"first {heads} of {wl.n_q_heads} query heads, all {wl.q_len} rows "
                   f"({flop / 1e9:.2f} GFLOP algorithmic) in {t_used:.1f} s; numpy float64, "
                   f"dense score matrix then mask",
         "seconds": round(t_used, 3),
@@ -139,29 +140,37 @@ def main() -> int:
     dev = torch.device("cuda:0")
     q, k, v = make_inputs(wl)
     dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
-    out = torch.empty((wl.seq_len, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
-    plan = fa.fa_prefill_plan(wl.n_q_heads, wl.n_kv_heads, wl.seq_len, wl.head_dim, int(wl.causal))
-
+    out = torch.empty((wl.q_len, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream(device=dev)
     # One step = one call of the C entry point (argument marshalling done once,
     # so the timed loop is not bound by Python-side checks).
-    call_args = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), wl.n_q_heads,
-                 wl.n_kv_heads, wl.seq_len, wl.head_dim, SCALE, int(wl.causal), stream.cuda_stream)
+    if wl.chunked:
+        plan = fa.fa_prefill_chunk_plan(wl.n_q_heads, wl.n_kv_heads, wl.q_len, wl.seq_len, wl.head_dim,
+                                        int(wl.causal))
+        entry = fa.fa_prefill_chunk
+        call_args = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), wl.n_q_heads,
+                     wl.n_kv_heads, wl.q_len, wl.seq_len, wl.head_dim, SCALE, int(wl.causal),
+                     stream.cuda_stream)
+    else:
+        plan = fa.fa_prefill_plan(wl.n_q_heads, wl.n_kv_heads, wl.seq_len, wl.head_dim, int(wl.causal))
+        entry = fa.fa_prefill
+        call_args = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), wl.n_q_heads,
+                     wl.n_kv_heads, wl.seq_len, wl.head_dim, SCALE, int(wl.causal), stream.cuda_stream)
     fa.attention(dq, dk, dv, SCALE, wl.causal, out=out, stream=stream)  # checked call first
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
-            fa.fa_prefill(*call_args)
+            entry(*call_args)
         stream.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record(stream)
-        statuses = [fa.fa_prefill(*call_args) for _ in range(args.steps)]
+        statuses = [entry(*call_args) for _ in range(args.steps)]
         end.record(stream)
         end.synchronize()
         torch.cuda.synchronize()
     if any(statuses):
-        print(f"bench.py: fa_prefill returned {set(statuses)}", file=sys.stderr)
+        print(f"bench.py: the entry point returned {set(statuses)}", file=sys.stderr)
         return 1
     region_ms = start.elapsed_time(end)
     ms_per_step = region_ms / args.steps
@@ -171,7 +180,7 @@ def main() -> int:
     min_bytes = (q.numel() + k.numel() + v.numel()) * 2 + out.numel() * 4
     line = {
         "metric": "causal FA prefill TFLOP/s + % f16 MFMA peak (S=2659, 32 heads, hd=128)"
-        if key == HEADLINE else f"causal FA prefill TFLOP/s ({wl.name})",
+        if key == HEADLINE else f"causal FA {'chunked ' if wl.chunked else ''}prefill TFLOP/s ({wl.name})",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -17,20 +17,42 @@
  * Grouped-query attention uses consecutive groups: query head h reads
  * key/value head hk = h / (n_q_heads / n_kv_heads).
  *
+ * Chunked prefill (fa_prefill_chunk).  q_len new tokens appended to a KV
+ * cache that already holds kv_len - q_len tokens: k and v hold all kv_len
+ * tokens (the chunk's own K/V are the last q_len rows) and query row i sits
+ * at sequence position kv_len - q_len + i, so with causal != 0 it sees keys
+ * j <= kv_len - q_len + i.  This is the pages' kernel reading: its validity
+ * test compares each key with the query's position and with the end of the
+ * stored KV range ("28 · r23", §3.2), and the K/V producer writes each
+ * token at its position ("11 · P5 — prefill gap session", §3.2).  With
+ * q_len == kv_len it is exactly fa_prefill.
+ *
  * Precision.  f16 inputs, f32 accumulation in the matrix cores, the softmax
  * in f32 registers, probabilities rounded to f16 (round to nearest even) as
  * the operand of P.V, f32 output.
  *
  * Layout.  All tensors are dense, token-major, row-major:
- *     q   f16 [seq_len][n_q_heads][head_dim]
- *     k   f16 [seq_len][n_kv_heads][head_dim]
- *     v   f16 [seq_len][n_kv_heads][head_dim]
- *     out f32 [seq_len][n_q_heads][head_dim]
+ *     q   f16 [seq_len][n_q_heads][head_dim]     (chunk: [q_len][...])
+ *     k   f16 [seq_len][n_kv_heads][head_dim]    (chunk: [kv_len][...])
+ *     v   f16 [seq_len][n_kv_heads][head_dim]    (chunk: [kv_len][...])
+ *     out f32 [seq_len][n_q_heads][head_dim]     (chunk: [q_len][...])
  * (so one token's row of one head is head_dim contiguous elements).
  *
  * Ownership.  q, k, v and out are device memory owned by the caller; the
- * library keeps no reference after the call returns and allocates nothing.
- * out must not overlap q, k or v.
+ * library keeps no reference to them after the call returns.  out must not
+ * overlap q, k or v.
+ *
+ * Workspace.  A launch whose grid would leave work-group slots idle (a short
+ * chunk over a long KV cache: fa_plan.kv_splits > 1) splits each query tile's
+ * key range over several work-groups and needs device scratch of
+ * fa_plan.workspace_bytes for their partial results.  The library owns it:
+ * one block per (device, stream), allocated and zeroed by the first call on
+ * that pair that needs it, grown by a later call that needs more (after
+ * synchronising that stream), and kept until fa_prefill_free_workspaces.
+ * Calls on one stream use it in stream order; calls on different streams
+ * never share a block.  A call that needs a new or larger block must
+ * therefore not be made during HIP graph capture.  Whole-sequence prefills
+ * that fill the device never split and never allocate.
  *
  * Execution.  fa_prefill enqueues one kernel on `stream` (a hipStream_t;
  * NULL = the null stream) and returns without waiting; the caller
@@ -49,17 +71,19 @@ extern "C" {
 #endif
 
 typedef enum fa_status {
-    FA_OK = 0,            /* success (seq_len == 0 is a successful no-op)         */
+    FA_OK = 0,            /* success (seq_len / q_len == 0 is a successful no-op) */
     FA_ERR_NULL = 1,      /* q, k, v or out is NULL (with seq_len > 0)             */
-    FA_ERR_SHAPE = 2,     /* seq_len < 0, heads <= 0, n_q_heads % n_kv_heads != 0,
-                             or a size that overflows the launch grid              */
+    FA_ERR_SHAPE = 2,     /* a length < 0, kv_len < q_len, heads <= 0,
+                             n_q_heads % n_kv_heads != 0, or a size that overflows
+                             the launch grid                                       */
     FA_ERR_HEAD_DIM = 3,  /* head_dim != 128                                       */
     FA_ERR_SCALE = 4,     /* scale is NaN or infinite                              */
     FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                      */
     FA_ERR_RESOURCE = 6,  /* the launch plan exceeds a device limit (LDS bytes)     */
     FA_ERR_LAUNCH = 7,    /* the HIP runtime reported an error at launch           */
     FA_ERR_ALIAS = 8,     /* out overlaps q, k or v                                */
-    FA_ERR_DEVICE = 9     /* no usable device, or the device is not gfx950         */
+    FA_ERR_DEVICE = 9,    /* no usable device, or the device is not gfx950         */
+    FA_ERR_WORKSPACE = 10 /* the library could not allocate or release its workspace */
 } fa_status;
 
 /* The only head dimension the kernel is built for (the pages' model uses
@@ -72,15 +96,17 @@ typedef struct fa_plan {
     int kv_tile;             /* key/value rows per LDS tile                       */
     int waves_per_group;     /* 64-lane wavefronts per work-group                 */
     int threads_per_group;   /* waves_per_group * 64                              */
-    int kv_splits;           /* wave groups per work-group, each taking a
-                                contiguous share of the query tile's KV tiles     */
-    int n_q_tiles;           /* ceil(seq_len / q_tile)                            */
-    long long n_groups;      /* work-groups launched: n_q_tiles * n_q_heads       */
-    int stages;              /* K/V tiles resident in LDS per wave group          */
-    int lds_bytes;           /* LDS per work-group: the sum of its planes         */
-    int lds_k_bytes;         /* K planes: kv_splits x stages x [kv_tile][head_dim] f16 */
-    int lds_v_bytes;         /* V planes: kv_splits x stages x [kv_tile][head_dim] f16 */
+    int kv_splits;           /* work-groups sharing one query tile's key range
+                                (split-KV; 1 = no split)                          */
+    int n_q_tiles;           /* ceil(q_len / q_tile)                              */
+    long long n_groups;      /* work-groups launched: n_q_tiles * n_q_heads * kv_splits */
+    int stages;              /* K/V tiles resident in LDS                          */
+    int lds_bytes;           /* LDS per work-group: the sum of its planes (K, V and
+                                a 16-byte flag)                                    */
+    int lds_k_bytes;         /* K planes: stages x [kv_tile][head_dim] f16         */
+    int lds_v_bytes;         /* V planes: stages x [kv_tile][head_dim] f16         */
     long long kv_tiles_visited; /* KV tiles the grid visits (causal tiles skipped) */
+    long long workspace_bytes;  /* library-owned device scratch the call needs (0: none) */
 } fa_plan;
 
 /*
@@ -101,13 +127,38 @@ int fa_prefill(const void* q, const void* k, const void* v, float* out,
                float scale, int causal, void* stream);
 
 /*
- * Compute the launch plan fa_prefill would use, without touching the GPU.
+ * Enqueue chunked prefill attention: q_len queries at positions
+ * kv_len - q_len .. kv_len - 1 over kv_len keys (see "Chunked prefill").
+ * Arguments as fa_prefill, with
+ *   q_len      >= 0 (0: nothing is launched, FA_OK); q and out hold q_len rows
+ *   kv_len     >= q_len; k and v hold kv_len rows
+ * kv_len < q_len is FA_ERR_SHAPE.  Returns FA_OK or an fa_status error;
+ * nothing is enqueued on error.
+ */
+int fa_prefill_chunk(const void* q, const void* k, const void* v, float* out,
+                     int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim,
+                     float scale, int causal, void* stream);
+
+/*
+ * Compute the launch plan fa_prefill would use, without touching the GPU, for
+ * an MI355X (256 compute units; fa_prefill plans for the current device).
  * Validates the shape arguments exactly as fa_prefill does (pointers aside).
  * max_lds_bytes: the device's LDS limit per work-group (0 = do not check).
  * plan: caller-owned output, written on FA_OK.
  */
 int fa_prefill_plan(int n_q_heads, int n_kv_heads, int seq_len, int head_dim,
                     int causal, int max_lds_bytes, fa_plan* plan);
+
+/* The plan fa_prefill_chunk would use (same validation, no GPU). */
+int fa_prefill_chunk_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim,
+                          int causal, int max_lds_bytes, fa_plan* plan);
+
+/*
+ * Release every workspace block the library holds (see "Workspace"), after
+ * waiting for the work queued on each block's device.  Later calls allocate
+ * again as needed.  Returns FA_OK or FA_ERR_WORKSPACE.
+ */
+int fa_prefill_free_workspaces(void);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_prefill_strerror(int status);

@@ -10,6 +10,9 @@ from .binding import (
     FaPlan,
     attention,
     fa_prefill,
+    fa_prefill_chunk,
+    fa_prefill_chunk_plan,
+    fa_prefill_free_workspaces,
     fa_prefill_last_error,
     fa_prefill_plan,
     fa_prefill_strerror,
@@ -22,6 +25,9 @@ __all__ = [
     "FaPlan",
     "attention",
     "fa_prefill",
+    "fa_prefill_chunk",
+    "fa_prefill_chunk_plan",
+    "fa_prefill_free_workspaces",
     "fa_prefill_last_error",
     "fa_prefill_plan",
     "fa_prefill_strerror",

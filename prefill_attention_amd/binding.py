@@ -25,9 +25,11 @@ STATUS_NAMES = {
     7: "FA_ERR_LAUNCH",
     8: "FA_ERR_ALIAS",
     9: "FA_ERR_DEVICE",
+    10: "FA_ERR_WORKSPACE",
 }
 # Every symbol include/fa_prefill.h declares.
-EXPORTED = ("fa_prefill", "fa_prefill_plan", "fa_prefill_strerror", "fa_prefill_last_error")
+EXPORTED = ("fa_prefill", "fa_prefill_chunk", "fa_prefill_plan", "fa_prefill_chunk_plan",
+            "fa_prefill_free_workspaces", "fa_prefill_strerror", "fa_prefill_last_error")
 
 
 class FaPlan(ctypes.Structure):
@@ -46,6 +48,7 @@ class FaPlan(ctypes.Structure):
         ("lds_k_bytes", ctypes.c_int),
         ("lds_v_bytes", ctypes.c_int),
         ("kv_tiles_visited", ctypes.c_longlong),
+        ("workspace_bytes", ctypes.c_longlong),
     ]
 
     def as_dict(self) -> dict:
@@ -80,11 +83,24 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
         ]
+        lib.fa_prefill_chunk.restype = ctypes.c_int
+        lib.fa_prefill_chunk.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
+        ]
+        lib.fa_prefill_chunk_plan.restype = ctypes.c_int
+        lib.fa_prefill_chunk_plan.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.POINTER(FaPlan),
+        ]
         lib.fa_prefill_plan.restype = ctypes.c_int
         lib.fa_prefill_plan.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.POINTER(FaPlan),
         ]
+        lib.fa_prefill_free_workspaces.restype = ctypes.c_int
+        lib.fa_prefill_free_workspaces.argtypes = []
         lib.fa_prefill_strerror.restype = ctypes.c_char_p
         lib.fa_prefill_strerror.argtypes = [ctypes.c_int]
         lib.fa_prefill_last_error.restype = ctypes.c_char_p
@@ -108,6 +124,24 @@ def fa_prefill(q, k, v, out, n_q_heads: int, n_kv_heads: int, seq_len: int, head
                           int(head_dim), float(scale), int(causal), stream)
 
 
+def fa_prefill_chunk(q, k, v, out, n_q_heads: int, n_kv_heads: int, q_len: int, kv_len: int,
+                     head_dim: int, scale: float, causal: int, stream) -> int:
+    """Same arguments as the C function; pointers as ints (or None), returns the status."""
+    lib = load_library()
+    return lib.fa_prefill_chunk(q, k, v, out, int(n_q_heads), int(n_kv_heads), int(q_len), int(kv_len),
+                                int(head_dim), float(scale), int(causal), stream)
+
+
+def fa_prefill_chunk_plan(n_q_heads: int, n_kv_heads: int, q_len: int, kv_len: int, head_dim: int,
+                          causal: int, max_lds_bytes: int = 0) -> FaPlan:
+    """Launch plan of a chunked call (no GPU); raises FaError on invalid shapes."""
+    lib = load_library()
+    plan = FaPlan()
+    _check(lib.fa_prefill_chunk_plan(int(n_q_heads), int(n_kv_heads), int(q_len), int(kv_len),
+                                     int(head_dim), int(causal), int(max_lds_bytes), ctypes.byref(plan)))
+    return plan
+
+
 def fa_prefill_plan(n_q_heads: int, n_kv_heads: int, seq_len: int, head_dim: int, causal: int,
                     max_lds_bytes: int = 0) -> FaPlan:
     """Launch plan (no GPU); raises FaError on invalid shapes."""
@@ -116,6 +150,11 @@ def fa_prefill_plan(n_q_heads: int, n_kv_heads: int, seq_len: int, head_dim: int
     _check(lib.fa_prefill_plan(int(n_q_heads), int(n_kv_heads), int(seq_len), int(head_dim),
                                int(causal), int(max_lds_bytes), ctypes.byref(plan)))
     return plan
+
+
+def fa_prefill_free_workspaces() -> None:
+    """Release the library's workspace blocks (waits for their devices)."""
+    _check(load_library().fa_prefill_free_workspaces())
 
 
 def fa_prefill_strerror(status: int) -> str:
@@ -127,9 +166,11 @@ def fa_prefill_last_error() -> str:
 
 
 def attention(q, k, v, scale: float, causal: bool = True, out=None, stream=None):
-    """Torch-facing call: q [S, Hq, 128] f16, k/v [S, Hkv, 128] f16 on one GPU.
+    """Torch-facing call: q [Q, Hq, 128] f16, k/v [S, Hkv, 128] f16 on one GPU.
 
-    Allocates ``out`` (f32 [S, Hq, 128]) unless given, enqueues the kernel on
+    Q == S is a whole prefill (fa_prefill); Q < S is a chunk of Q new tokens
+    at positions S - Q .. S - 1 over a KV cache of S tokens (fa_prefill_chunk).
+    Allocates ``out`` (f32 [Q, Hq, 128]) unless given, enqueues the kernel on
     ``stream`` (default: torch's current stream) and returns ``out``.
     """
     import torch
@@ -143,21 +184,26 @@ def attention(q, k, v, scale: float, causal: bool = True, out=None, stream=None)
             raise ValueError(f"{name} must be on the GPU")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    S, n_q, hd = q.shape
-    if k.shape != v.shape or k.shape[0] != S or k.shape[2] != hd:
-        raise ValueError("k and v must be [seq_len, n_kv_heads, head_dim] matching q")
+    Q, n_q, hd = q.shape
+    S = k.shape[0]
+    if k.shape != v.shape or S < Q or k.shape[2] != hd:
+        raise ValueError("k and v must be [kv_len, n_kv_heads, head_dim] with kv_len >= q's length")
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k, v must be on the same device")
     if out is None:
-        out = torch.empty((S, n_q, hd), dtype=torch.float32, device=q.device)
-    elif out.dtype != torch.float32 or out.shape != (S, n_q, hd) or not out.is_contiguous() \
+        out = torch.empty((Q, n_q, hd), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or out.shape != (Q, n_q, hd) or not out.is_contiguous() \
             or out.device != q.device:
-        raise ValueError("out must be contiguous float32 [seq_len, n_q_heads, head_dim] on q's device")
+        raise ValueError("out must be contiguous float32 [q_len, n_q_heads, head_dim] on q's device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
     with torch.cuda.device(q.device):
-        status = fa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), n_q,
-                            k.shape[1], S, hd, scale, 1 if causal else 0, handle)
+        if Q == S:
+            status = fa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), n_q,
+                                k.shape[1], S, hd, scale, 1 if causal else 0, handle)
+        else:
+            status = fa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), n_q,
+                                      k.shape[1], Q, S, hd, scale, 1 if causal else 0, handle)
     _check(status)
     return out

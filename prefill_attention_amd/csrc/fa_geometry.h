@@ -17,7 +17,13 @@ constexpr int kThreads = kWaves * kWaveSize;
 constexpr int kQTile = kWaves * kQRowsPerWave;  // 128 query rows per work-group
 constexpr int kKvTile = 64;            // key/value rows per LDS tile
 constexpr int kStages = 2;             // LDS tiles in flight (double buffer)
-constexpr int kGroups = 1;             // wave groups splitting one query tile's KV range
+constexpr int kGroupsPerCu = 2;        // resident work-groups per CU (VGPRs: 2 waves per SIMD)
+
+// Split-KV for grids that would leave work-group slots idle (a short chunk over
+// a long KV cache): each query tile's key range is divided over up to
+// kMaxSplits work-groups, each part at least kMinSplitTiles key tiles long.
+constexpr int kMaxSplits = 8;
+constexpr int kMinSplitTiles = 4;
 
 // LDS planes.  K and V tiles are both stored key-major with unpadded
 // 256-byte rows; the sixteen 16-byte chunks of a row are permuted by
@@ -27,7 +33,8 @@ constexpr int kRowBytes = kHeadDim * 2;
 constexpr int kTileBytes = kKvTile * kRowBytes;           // one K or one V tile: 16 KiB
 constexpr int kLdsKBytes = kStages * kTileBytes;
 constexpr int kLdsVBytes = kStages * kTileBytes;
-constexpr int kLdsBytes = kLdsKBytes + kLdsVBytes;       // 64 KiB
+constexpr int kLdsMiscBytes = 16;                         // the merge-election flag
+constexpr int kLdsBytes = kLdsKBytes + kLdsVBytes + kLdsMiscBytes;  // 64 KiB + 16 B
 
 // Work-groups are dispatched round-robin over the 8 XCDs of an MI355X.
 constexpr int kXcds = 8;

@@ -10,12 +10,23 @@ namespace fa {
 int fail(int status, const char* fmt, ...);
 void clear_error();
 
-// Shape validation + launch plan (no GPU).  max_lds_bytes <= 0 skips the LDS check.
-int make_plan(int n_q_heads, int n_kv_heads, int seq_len, int head_dim, int causal,
-              int max_lds_bytes, fa_plan* plan);
+// Shape validation + launch plan (no GPU) for q_len queries at the last
+// q_len of kv_len positions, on a device with n_cus compute units (<= 0:
+// 256).  max_lds_bytes <= 0 skips the LDS check.
+int make_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim, int causal,
+              int max_lds_bytes, int n_cus, fa_plan* plan);
 
-// Pointer, alignment, aliasing and scale checks of one fa_prefill call.
+// Workspace of a split-KV launch, laid out for a block's capacity (not for the
+// plan using it), so that every plan fitting a block finds the same zeroed
+// counters: [items] int arrival counters, then [parts][kQTile] f32
+// log-weights, then [parts][kQTile][kHeadDim] f32 normalised partial outputs
+// (a part is one split of one query tile of one head).
+long long workspace_lw_offset(long long cap_items);
+long long workspace_o_offset(long long cap_items, long long cap_parts);
+long long workspace_bytes(long long cap_items, long long cap_parts);
+
+// Pointer, alignment, aliasing and scale checks of one call.
 int validate_call(const void* q, const void* k, const void* v, const float* out, int n_q_heads,
-                  int n_kv_heads, int seq_len, int head_dim, float scale);
+                  int n_kv_heads, int q_len, int kv_len, int head_dim, float scale);
 
 }  // namespace fa

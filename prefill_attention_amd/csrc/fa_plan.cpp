@@ -31,15 +31,51 @@ int fail(int status, const char* fmt, ...) {
 
 void clear_error() { g_last_error[0] = '\0'; }
 
-// KV tiles a work-group starting at query row q0 visits.
-static long long tiles_for_group(int q0, int seq_len, bool causal) {
-    long long kv_end = causal ? (q0 + kQTile < seq_len ? q0 + kQTile : seq_len) : seq_len;
+// KV tiles a work-group starting at query row q0 visits (query row r is at
+// position kv_len - q_len + r).
+static long long tiles_for_group(long long q0, long long q_off, long long kv_len, bool causal) {
+    const long long last = q_off + q0 + kQTile;
+    const long long kv_end = causal ? (last < kv_len ? last : kv_len) : kv_len;
     return (kv_end + kKvTile - 1) / kKvTile;
 }
 
-int make_plan(int n_q_heads, int n_kv_heads, int seq_len, int head_dim, int causal,
-              int max_lds_bytes, fa_plan* plan) {
-    if (seq_len < 0) return fail(FA_ERR_SHAPE, "seq_len %d < 0", seq_len);
+long long workspace_lw_offset(long long cap_items) { return ((cap_items * 4 + 255) / 256) * 256; }
+long long workspace_o_offset(long long cap_items, long long cap_parts) {
+    return workspace_lw_offset(cap_items) + cap_parts * (long long)kQTile * 4;
+}
+long long workspace_bytes(long long cap_items, long long cap_parts) {
+    return cap_parts == 0 ? 0
+                          : workspace_o_offset(cap_items, cap_parts) + cap_parts * (long long)kQTile * kHeadDim * 4;
+}
+
+// Split-KV count for a launch of `items` query tiles.  Splitting pays only
+// when the grid leaves resident work-group slots idle (a whole-sequence
+// prefill that fills the slots measured slower when split: every extra
+// work-group adds its start-up latency).  Each part must begin at or before
+// the first query position of its tile, so that every query row sees a key
+// in every part (the parts share out the tiles that start at or before that
+// position; the last part also takes the diagonal and tail tiles): with the
+// causal mask this needs a KV cache in front of the chunk.  All parts of a
+// tile must run on one XCD (they meet through its L2), which the XCD-wise
+// head assignment guarantees when the head count is a multiple of 8.
+static int choose_splits(long long items, long long q_off, long long kv_len, bool causal, int n_q_heads,
+                         int n_cus) {
+    const long long slots = (long long)kGroupsPerCu * n_cus;
+    if (items <= 0 || items * 2 > slots || n_q_heads % kXcds != 0) return 1;
+    // tiles shared out, for the tile with the fewest (the first query tile)
+    const long long shared = causal ? q_off / kKvTile + 1 : (kv_len + kKvTile - 1) / kKvTile;
+    long long n = slots / items;
+    n = n < kMaxSplits ? n : kMaxSplits;
+    n = n < shared / kMinSplitTiles ? n : shared / kMinSplitTiles;
+    return n >= 2 ? (int)n : 1;
+}
+
+int make_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim, int causal,
+              int max_lds_bytes, int n_cus, fa_plan* plan) {
+    if (q_len < 0) return fail(FA_ERR_SHAPE, "q_len %d < 0", q_len);
+    if (kv_len < q_len)
+        return fail(FA_ERR_SHAPE, "kv_len %d < q_len %d (the queries are the last q_len of kv_len tokens)",
+                    kv_len, q_len);
     if (n_q_heads <= 0 || n_kv_heads <= 0)
         return fail(FA_ERR_SHAPE, "head counts must be positive (n_q_heads %d, n_kv_heads %d)",
                     n_q_heads, n_kv_heads);
@@ -52,51 +88,57 @@ int make_plan(int n_q_heads, int n_kv_heads, int seq_len, int head_dim, int caus
                     n_kv_heads);
     if (head_dim != kHeadDim)
         return fail(FA_ERR_HEAD_DIM, "head_dim %d unsupported (only %d)", head_dim, kHeadDim);
-    long long n_q_tiles = ((long long)seq_len + kQTile - 1) / kQTile;
+    long long n_q_tiles = ((long long)q_len + kQTile - 1) / kQTile;
     long long n_groups = n_q_tiles * (long long)n_q_heads;
     if (n_groups > INT_MAX)
         return fail(FA_ERR_SHAPE, "grid of %lld work-groups exceeds the launch limit", n_groups);
     // element offsets of the largest tensor must fit a signed 64-bit range
-    if ((long long)seq_len * n_q_heads > (LLONG_MAX / 4) / kHeadDim)
+    if ((long long)kv_len * n_q_heads > (LLONG_MAX / 4) / kHeadDim)
         return fail(FA_ERR_SHAPE, "tensor too large");
     if (max_lds_bytes > 0 && kLdsBytes > max_lds_bytes)
         return fail(FA_ERR_RESOURCE, "kernel needs %d B of LDS per work-group, device allows %d",
                     kLdsBytes, max_lds_bytes);
+    if (n_cus <= 0) n_cus = 256;
+    const long long items = n_q_tiles * (long long)n_q_heads;
+    const int splits = choose_splits(items, (long long)kv_len - q_len, kv_len, causal != 0, n_q_heads, n_cus);
+    if (items * splits > INT_MAX)
+        return fail(FA_ERR_SHAPE, "grid of %lld work-groups exceeds the launch limit", items * splits);
     if (plan) {
         plan->q_tile = kQTile;
         plan->kv_tile = kKvTile;
         plan->waves_per_group = kWaves;
         plan->threads_per_group = kThreads;
-        plan->kv_splits = kGroups;
+        plan->kv_splits = splits;
         plan->n_q_tiles = (int)n_q_tiles;
-        plan->n_groups = n_groups;
+        plan->n_groups = items * splits;
+        plan->workspace_bytes = splits > 1 ? workspace_bytes(items, items * splits) : 0;
         plan->stages = kStages;
         plan->lds_bytes = kLdsBytes;
         plan->lds_k_bytes = kLdsKBytes;
         plan->lds_v_bytes = kLdsVBytes;
         long long tiles = 0;
         for (long long t = 0; t < n_q_tiles; ++t)
-            tiles += tiles_for_group((int)(t * kQTile), seq_len, causal != 0);
+            tiles += tiles_for_group(t * kQTile, (long long)kv_len - q_len, kv_len, causal != 0);
         plan->kv_tiles_visited = tiles * n_q_heads;
     }
     return FA_OK;
 }
 
 int validate_call(const void* q, const void* k, const void* v, const float* out, int n_q_heads,
-                  int n_kv_heads, int seq_len, int head_dim, float scale) {
-    if (seq_len > 0 && (!q || !k || !v || !out))
+                  int n_kv_heads, int q_len, int kv_len, int head_dim, float scale) {
+    if (q_len > 0 && (!q || !k || !v || !out))
         return fail(FA_ERR_NULL, "a tensor pointer is NULL");
     if (!std::isfinite(scale)) return fail(FA_ERR_SCALE, "scale is not finite");
-    if (seq_len <= 0) return FA_OK;
+    if (q_len <= 0) return FA_OK;
     auto misaligned = [](const void* p) { return (reinterpret_cast<unsigned long long>(p) & 15ull) != 0; };
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out))
         return fail(FA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
     // overlap of out with an input
-    const unsigned long long S = (unsigned long long)seq_len;
+    const unsigned long long Q = (unsigned long long)q_len, S = (unsigned long long)kv_len;
     const unsigned long long ob = reinterpret_cast<unsigned long long>(out);
-    const unsigned long long oe = ob + S * n_q_heads * head_dim * 4ull;
+    const unsigned long long oe = ob + Q * n_q_heads * head_dim * 4ull;
     struct Span { const void* p; unsigned long long bytes; } in[3] = {
-        {q, S * n_q_heads * head_dim * 2ull},
+        {q, Q * n_q_heads * head_dim * 2ull},
         {k, S * n_kv_heads * head_dim * 2ull},
         {v, S * n_kv_heads * head_dim * 2ull}};
     for (const Span& s : in) {
@@ -113,14 +155,21 @@ extern "C" {
 int fa_prefill_plan(int n_q_heads, int n_kv_heads, int seq_len, int head_dim, int causal,
                     int max_lds_bytes, fa_plan* plan) {
     fa::clear_error();
-    return fa::make_plan(n_q_heads, n_kv_heads, seq_len, head_dim, causal, max_lds_bytes, plan);
+    return fa::make_plan(n_q_heads, n_kv_heads, seq_len, seq_len, head_dim, causal, max_lds_bytes, 0,
+                         plan);
+}
+
+int fa_prefill_chunk_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim,
+                          int causal, int max_lds_bytes, fa_plan* plan) {
+    fa::clear_error();
+    return fa::make_plan(n_q_heads, n_kv_heads, q_len, kv_len, head_dim, causal, max_lds_bytes, 0, plan);
 }
 
 const char* fa_prefill_strerror(int status) {
     switch (status) {
         case FA_OK: return "success";
         case FA_ERR_NULL: return "a tensor pointer is NULL";
-        case FA_ERR_SHAPE: return "invalid shape (sequence length, head counts or grid size)";
+        case FA_ERR_SHAPE: return "invalid shape (lengths, head counts or grid size)";
         case FA_ERR_HEAD_DIM: return "unsupported head_dim (only 128)";
         case FA_ERR_SCALE: return "scale is not finite";
         case FA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
@@ -128,6 +177,7 @@ const char* fa_prefill_strerror(int status) {
         case FA_ERR_LAUNCH: return "HIP runtime error at kernel launch";
         case FA_ERR_ALIAS: return "output overlaps an input";
         case FA_ERR_DEVICE: return "no usable gfx950 device";
+        case FA_ERR_WORKSPACE: return "workspace allocation or release failed";
         default: return "unknown fa_prefill status";
     }
 }

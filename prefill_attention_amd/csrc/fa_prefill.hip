@@ -16,7 +16,7 @@
 //
 //  * K and V tiles go from HBM/L2 straight into LDS with buffer loads that
 //    write LDS directly (no register staging).  The buffer descriptor's
-//    record count ends at the sequence end, so rows past seq_len read as
+//    record count ends at the last stored key, so rows past kv_len read as
 //    zeros in hardware (the pages zero-fill them explicitly, "53 · r50", §2).
 //    Two LDS stages: tile j+1 streams in while tile j is computed, with one
 //    work-group barrier per tile.
@@ -47,10 +47,15 @@
 //    not rescaled at all.  O/l is unchanged in exact arithmetic by the choice
 //    of reference, so the result is the same softmax.
 //
-//  * The validity predicate is "key <= query (causal) and key < seq_len",
-//    both bounds always applied (the pages' tail-tile lane-mask bug, "28 ·
-//    r23", §2.3), but only on tiles that touch the diagonal or the sequence
-//    end; every other tile runs unmasked.
+//  * The validity predicate is "key <= the query's position (causal) and
+//    key < kv_len", both bounds always applied (the pages' tail-tile
+//    lane-mask bug, "28 · r23", §2.3), but only on tiles that touch the
+//    diagonal or the end of the keys; every other tile runs unmasked.  Query
+//    row r is at position kv_len - q_len + r: the whole sequence for a
+//    prefill, the last q_len positions for a chunk appended to a KV cache
+//    (the pages compare keys with a query position against a stored-KV end,
+//    "28 · r23", §3.2, and write each token's K/V at its position, "11 · P5",
+//    §3.2).
 //
 //  * Work-group order: the heaviest query tiles first; when the head count is
 //    a multiple of 8, the 8 XCDs (which receive work-groups round-robin) each
@@ -58,9 +63,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "fa_geometry.h"
 #include "fa_internal.h"
@@ -115,18 +123,18 @@ __device__ __forceinline__ int acc_key(int kb, int i, int g) {
     return 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
 }
 
-// Copy key/value rows [kt, kt + 64) of head hk from src (f16 [S][n_kv][128])
-// into an LDS tile; this wavefront copies rows 16*wave .. 16*wave + 15, four
+// Copy key/value rows [kt, kt + 64) of head hk from src (f16
+// [kv_len][n_kv][128]) into an LDS tile; this wavefront copies rows 16*wave .. 16*wave + 15, four
 // rows (1 KiB) per instruction.  Lane i of an instruction fills physical
 // chunk i % 16 of its row, so it loads logical chunk (i % 16) ^ swz(row).
 __device__ __forceinline__ void stage_tile(const _Float16* __restrict__ src, int n_kv, int hk,
-                                           int seq_len, int kt, char* tile, int wave, int lane) {
+                                           int kv_len, int kt, char* tile, int wave, int lane) {
     const uint32_t row_bytes = (uint32_t)n_kv * kRowBytes;
     const char* base = reinterpret_cast<const char*>(src) + (size_t)kt * row_bytes +
                        (size_t)hk * kRowBytes;
     // Bytes addressable from base: up to the end of the last valid row of
-    // this head, so rows >= seq_len fall outside the record and read as 0.
-    const long long valid = (long long)(seq_len - kt) * row_bytes - (long long)hk * kRowBytes;
+    // this head, so rows >= kv_len fall outside the record and read as 0.
+    const long long valid = (long long)(kv_len - kt) * row_bytes - (long long)hk * kRowBytes;
     const long long cap = (long long)kKvTile * row_bytes;
     const uint32_t n_records = (uint32_t)(valid < cap ? valid : cap);
     const __amdgpu_buffer_rsrc_t rsrc =
@@ -181,24 +189,27 @@ struct TileScores {
     floatx16 b[2];
 };
 
-// Mask the scores of tile t: -inf where the key is past the sequence or (causal)
-// after the query.  Only tiles on the diagonal or at the sequence end need it.
+// Mask the scores of tile t: -inf where the key is past the stored keys or
+// (causal) after the query's position.  Only tiles on the diagonal or at the
+// end of the keys need it.
 template <bool CAUSAL>
-__device__ __forceinline__ void mask_scores(TileScores& s, int t, int my_q, int seq_len, int g) {
+__device__ __forceinline__ void mask_scores(TileScores& s, int t, int q_pos, int kv_len, int g) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int key = t * kKvTile + acc_key(kb, i, g);
-            const bool ok = key < seq_len && (!CAUSAL || key <= my_q);
+            const bool ok = key < kv_len && (!CAUSAL || key <= q_pos);
             s.b[kb][i] = ok ? s.b[kb][i] : -INFINITY;
         }
 }
 
+// Whether tile t needs the mask for a wavefront whose first query is at
+// position pos_w.
 template <bool CAUSAL>
-__device__ __forceinline__ bool tile_needs_mask(int t, int qw, int seq_len) {
-    return (t * kKvTile + kKvTile > seq_len) ||
-           (CAUSAL && t * kKvTile + kKvTile - 1 > qw);
+__device__ __forceinline__ bool tile_needs_mask(int t, int pos_w, int kv_len) {
+    return (t * kKvTile + kKvTile > kv_len) ||
+           (CAUSAL && t * kKvTile + kKvTile - 1 > pos_w);
 }
 
 // Phase A of the tile pipeline, as 16 explicit issue slots.  Slot i
@@ -323,12 +334,15 @@ __device__ __forceinline__ void maybe_rescale(float mt, float& m_ref, float& l_p
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k, const _Float16* __restrict__ v,
-    float* __restrict__ out, int seq_len, int n_q_heads, int n_kv_heads, int n_q_tiles, float c2,
-    int q_mode) {
+    float* __restrict__ out, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int n_q_tiles,
+    float c2, int q_mode, int n_splits, int* __restrict__ ws_ctr, float* __restrict__ ws_lw,
+    float* __restrict__ ws_o) {
     __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
-    // K tile t lives in kbuf(t), V tile t in vbuf(t): two buffers each.
+    // K tile i lives in kbuf(i), V tile i in vbuf(i): two buffers each (i counts
+    // the tiles of this work-group's key range).
     char* const kstage = lds;
     char* const vstage = lds + kLdsKBytes;
+    int* const merge_flag = reinterpret_cast<int*>(lds + kLdsKBytes + kLdsVBytes);
     auto kbuf = [&](int t) { return kstage + (t & 1) * kTileBytes; };
     auto vbuf = [&](int t) { return vstage + (t & 1) * kTileBytes; };
 
@@ -338,16 +352,20 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const int l32 = lane & 31;
     const int g = lane >> 5;
 
-    // Work-group -> (head, query tile): heaviest query tiles first; with a
-    // head count divisible by the XCD count, XCD x (= blockIdx % 8) owns heads
-    // [x*H/8, (x+1)*H/8).
+    // Work-group -> (head, query tile, key-range part): heaviest query tiles
+    // first; with a head count divisible by the XCD count, XCD x (= blockIdx
+    // % 8) owns heads [x*H/8, (x+1)*H/8), so one kv head's K/V stays in one
+    // L2 and all parts of a split query tile meet in that L2.  (Other head
+    // counts are never split.)
     const int b = blockIdx.x;
-    int h, rank;
+    int h, rank, split = 0;
     if ((n_q_heads % kXcds) == 0) {
         const int per_xcd = n_q_heads / kXcds;
         const int local = b / kXcds;
-        h = (b % kXcds) * per_xcd + local % per_xcd;
-        rank = local / per_xcd;
+        rank = local / (per_xcd * n_splits);
+        const int rem = local % (per_xcd * n_splits);
+        split = rem / per_xcd;
+        h = (b % kXcds) * per_xcd + rem % per_xcd;
     } else {
         h = b % n_q_heads;
         rank = b / n_q_heads;
@@ -356,22 +374,39 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const int hk = h / (n_q_heads / n_kv_heads);
     const int q0 = qt * kQTile;
     const int qw = q0 + wave * kQRowsPerWave;
-    const int my_q = qw + l32;
+    const int my_q = qw + l32;  // query row (index into q and out)
+    // Query row r sits at sequence position q_off + r: a chunk of q_len new
+    // tokens follows kv_len - q_len tokens already in the KV cache (q_off = 0
+    // for a whole prefill).
+    const int q_off = kv_len - q_len;
+    const int pos_w = q_off + qw;
+    const int q_pos = q_off + my_q;
 
-    const int kv_end = CAUSAL ? min(seq_len, q0 + kQTile) : seq_len;
-    const int n_tiles = (kv_end + kKvTile - 1) / kKvTile;
+    const int kv_end = CAUSAL ? min(kv_len, q_off + q0 + kQTile) : kv_len;
+    const int n_all = (kv_end + kKvTile - 1) / kKvTile;
+    // Key tiles [t_lo, t_lo + n_tiles) of this work-group.  A split tile's
+    // parts share out the tiles that start at or before the tile's first
+    // query position (so every query row sees a key in every part); the last
+    // part also takes the diagonal and tail tiles.
+    int t_lo = 0, n_tiles = n_all;
+    if (n_splits > 1) {
+        const int shared = CAUSAL ? (q_off + q0) / kKvTile + 1 : n_all;
+        t_lo = split * shared / n_splits;
+        n_tiles = (split == n_splits - 1 ? n_all : (split + 1) * shared / n_splits) - t_lo;
+    }
+    auto kv_row = [&](int i) { return (t_lo + i) * kKvTile; };
 
     // Staging schedule: K tile t is copied two tiles ahead of its use in
     // phase A, V tile t one tile ahead of its use in phase B.
-    stage_tile(k, n_kv_heads, hk, seq_len, 0, kbuf(0), wave, lane);
-    stage_tile(v, n_kv_heads, hk, seq_len, 0, vbuf(0), wave, lane);
-    if (n_tiles > 1) stage_tile(k, n_kv_heads, hk, seq_len, kKvTile, kbuf(1), wave, lane);
+    stage_tile(k, n_kv_heads, hk, kv_len, kv_row(0), kbuf(0), wave, lane);
+    stage_tile(v, n_kv_heads, hk, kv_len, kv_row(0), vbuf(0), wave, lane);
+    if (n_tiles > 1) stage_tile(k, n_kv_heads, hk, kv_len, kv_row(1), kbuf(1), wave, lane);
 
     // Q^T as the B operand: lane (l32, g) holds q[my_q][h][16t + 8g .. +8).
     // q_mode 1 negates Q (negative scale), 2 zeroes it (scale 0).
     half8 qb[8];
     {
-        const bool in = my_q < seq_len && q_mode != 2;
+        const bool in = my_q < q_len && q_mode != 2;
         const _Float16* qrow = q + ((size_t)my_q * n_q_heads + h) * kHeadDim + 8 * g;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
@@ -399,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     {
         half8 vf_unused[4];
         phase_a<false, true, false>(kbuf(0), qb, sa, sa, pb, l_part, m_ref, c2, l32, g, nullptr, vt_off, vf_unused);
-        if (tile_needs_mask<CAUSAL>(0, qw, seq_len)) mask_scores<CAUSAL>(sa, 0, my_q, seq_len, g);
+        if (tile_needs_mask<CAUSAL>(t_lo, pos_w, kv_len)) mask_scores<CAUSAL>(sa, t_lo, q_pos, kv_len, g);
         float mx = fmaxf(sa.b[0][0], sa.b[1][0]);
 #pragma unroll
         for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sa.b[0][i], sa.b[1][i]));
@@ -413,11 +448,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     auto step = [&](int j, TileScores& sc, TileScores& sn) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (j + 2 < n_tiles) stage_tile(k, n_kv_heads, hk, seq_len, (j + 2) * kKvTile, kbuf(j + 2), wave, lane);
-        stage_tile(v, n_kv_heads, hk, seq_len, (j + 1) * kKvTile, vbuf(j + 1), wave, lane);
+        if (j + 2 < n_tiles) stage_tile(k, n_kv_heads, hk, kv_len, kv_row(j + 2), kbuf(j + 2), wave, lane);
+        stage_tile(v, n_kv_heads, hk, kv_len, kv_row(j + 1), vbuf(j + 1), wave, lane);
         half8 vf[4];
         phase_a<true, true, true>(kbuf(j + 1), qb, sc, sn, pb, l_part, m_ref, c2, l32, g, vbuf(j), vt_off, vf);
-        if (tile_needs_mask<CAUSAL>(j + 1, qw, seq_len)) mask_scores<CAUSAL>(sn, j + 1, my_q, seq_len, g);
+        if (tile_needs_mask<CAUSAL>(t_lo + j + 1, pos_w, kv_len))
+            mask_scores<CAUSAL>(sn, t_lo + j + 1, q_pos, kv_len, g);
         const float mt = phase_b<true>(vbuf(j), pb, oacc, sn, c2, l32, g, vt_off, vf);
         maybe_rescale(mt, m_ref, l_part, oacc);
     };
@@ -442,31 +478,137 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
         last(j, sa);
     }
 
-    // Epilogue: O / l, rows < seq_len only.  Lane (l32, g), register i of
-    // block db holds head-dim 32*db + 8*(i/4) + 4*g + i%4.
+    // Epilogue, rows < q_len only.  Lane (l32, g), register i of block db
+    // holds head-dim 32*db + 8*(i/4) + 4*g + i%4.
     const float l_tot = pair_sum(l_part);
-    if (my_q < seq_len) {
-        const float inv = 1.0f / l_tot;
-        float* orow = out + ((size_t)my_q * n_q_heads + h) * kHeadDim + 4 * g;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    float* const orow = out + ((size_t)my_q * n_q_heads + h) * kHeadDim + 4 * g;
+    if (n_splits == 1) {
+        if (my_q < q_len) {
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const floatx4 o = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv,
+                                       oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv};
+                    *reinterpret_cast<floatx4*>(orow + 32 * db + 8 * jj) = o;
+                }
+        }
+        return;
+    }
+
+    // One part of a split query tile.  Publish its normalised output O / l
+    // and its log-weight lw = m + log2(l) (the softmax mass of its keys, in
+    // log2 units), then count arrivals; the last part to arrive combines all
+    // parts as out = sum_s w_s (O/l)_s / sum_s w_s with w_s = 2^(lw_s - max lw)
+    // -- the merge the online softmax applies between key tiles -- reading
+    // every part (its own included) from the workspace in part order, so the
+    // result does not depend on which part finished last.
+    const int item = h * n_q_tiles + qt;
+    const int row = wave * kQRowsPerWave + l32;
+    const size_t part0 = (size_t)item * n_splits;
+    if (my_q < q_len) {
+        float* const po = ws_o + ((part0 + split) * kQTile + row) * kHeadDim + 4 * g;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const floatx4 o = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv,
                                    oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv};
-                *reinterpret_cast<floatx4*>(orow + 32 * db + 8 * jj) = o;
+                *reinterpret_cast<floatx4*>(po + 32 * db + 8 * jj) = o;
             }
+        if (g == 0)
+            ws_lw[(part0 + split) * kQTile + row] =
+                l_tot > 0.0f ? m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    }
+    // All parts of this tile run on this XCD and meet in its L2: each wave
+    // waits until its stores have reached the L2 before the arrival is
+    // counted (an atomic performed in the L2), and the last part drops its
+    // CU's L1 lines before reading the others' results.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+        *merge_flag = __hip_atomic_fetch_add(ws_ctr + item, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*merge_flag != n_splits - 1) return;
+    asm volatile("buffer_inv sc0" ::: "memory");
+    if (tid == 0) __hip_atomic_store(ws_ctr + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (my_q < q_len) {
+        float wt[kMaxSplits];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < kMaxSplits; ++p) {
+            wt[p] = p < n_splits ? ws_lw[(part0 + p) * kQTile + row] : -INFINITY;
+            mx = fmaxf(mx, wt[p]);
+        }
+        float wsum = 0.0f;
+#pragma unroll
+        for (int p = 0; p < kMaxSplits; ++p) {
+            wt[p] = p < n_splits ? __builtin_amdgcn_exp2f(wt[p] - mx) : 0.0f;
+            wsum += wt[p];
+        }
+        const float norm = 1.0f / wsum;
+        // Two halves of the head dimension; in each, the parts' values are
+        // loaded four parts at a time so their latencies overlap, and every
+        // sum runs in part order.
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            floatx4 acc[2][4];
+#pragma unroll
+            for (int d = 0; d < 2; ++d)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[d][jj] = floatx4{};
+#pragma unroll
+            for (int p0 = 0; p0 < kMaxSplits; p0 += 4) {
+                if (p0 >= n_splits) break;
+                floatx4 x[4][2][4];
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                    const int p = p0 + pp;
+                    if (p < n_splits) {
+                        const float* po = ws_o + ((part0 + p) * kQTile + row) * kHeadDim + 4 * g;
+#pragma unroll
+                        for (int d = 0; d < 2; ++d)
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj)
+                                x[pp][d][jj] = *reinterpret_cast<const floatx4*>(po + 32 * (2 * hf + d) + 8 * jj);
+                    }
+                }
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                    const int p = p0 + pp;
+                    if (p >= n_splits) break;
+#pragma unroll
+                    for (int d = 0; d < 2; ++d)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[d][jj][e] += wt[p] * x[pp][d][jj][e];
+                        }
+                }
+            }
+#pragma unroll
+            for (int d = 0; d < 2; ++d)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    *reinterpret_cast<floatx4*>(orow + 32 * (2 * hf + d) + 8 * jj) = acc[d][jj] * norm;
+        }
     }
 }
 
-// Per-device check: gfx950 and the LDS limit, cached (0 unknown, 1 ok, else the error).
+// Per-device check: gfx950 and the LDS limit, cached (0 unknown, 1 ok, else
+// the error), with the device's compute-unit count.
 constexpr int kMaxDevices = 64;
 int g_device_state[kMaxDevices];
+int g_device_cus[kMaxDevices];
 
-int check_device(int dev) {
+int check_device(int dev, int* n_cus) {
     if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_DEVICE, "device index %d out of range", dev);
     int st = __atomic_load_n(&g_device_state[dev], __ATOMIC_ACQUIRE);
-    if (st == 1) return FA_OK;
+    if (st == 1) {
+        *n_cus = __atomic_load_n(&g_device_cus[dev], __ATOMIC_RELAXED);
+        return FA_OK;
+    }
     if (st > 1) return fail(st, "device %d is not usable (see first error)", dev);
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
@@ -478,29 +620,99 @@ int check_device(int dev) {
     else if ((size_t)kLdsBytes > prop.sharedMemPerBlock)
         result = fail(FA_ERR_RESOURCE, "kernel needs %d B of LDS, device allows %zu", kLdsBytes,
                       prop.sharedMemPerBlock);
+    __atomic_store_n(&g_device_cus[dev], prop.multiProcessorCount, __ATOMIC_RELAXED);
     __atomic_store_n(&g_device_state[dev], result == FA_OK ? 1 : result, __ATOMIC_RELEASE);
+    *n_cus = prop.multiProcessorCount;
     return result;
+}
+
+// Library-owned workspace blocks, one per (device, stream).  A block only
+// grows; it is zeroed when allocated and every kernel leaves its arrival
+// counters at zero again.  Its layout follows its capacity.
+struct WorkspaceBlock {
+    int dev;
+    void* stream;
+    char* ptr;
+    long long cap_items, cap_parts;
+};
+std::mutex g_ws_mu;
+std::vector<WorkspaceBlock> g_ws;
+
+struct Workspace {
+    int* ctr;
+    float* lw;
+    float* o;
+};
+
+int acquire_workspace(int dev, void* stream, long long items, long long parts, Workspace* ws) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    WorkspaceBlock* blk = nullptr;
+    for (WorkspaceBlock& w : g_ws)
+        if (w.dev == dev && w.stream == stream) blk = &w;
+    if (!blk || blk->cap_items < items || blk->cap_parts < parts) {
+        long long cap_items = items, cap_parts = parts;
+        if (blk) {
+            cap_items = std::max(cap_items, blk->cap_items);
+            cap_parts = std::max(cap_parts, blk->cap_parts);
+            // Earlier kernels on this stream may still use the smaller block.
+            if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess ||
+                hipFree(blk->ptr) != hipSuccess)
+                return fail(FA_ERR_WORKSPACE, "could not release the old workspace of device %d", dev);
+            blk->ptr = nullptr;
+            blk->cap_items = blk->cap_parts = 0;
+        }
+        const size_t bytes = (size_t)workspace_bytes(cap_items, cap_parts);
+        void* p = nullptr;
+        if (hipMalloc(&p, bytes) != hipSuccess)
+            return fail(FA_ERR_WORKSPACE, "hipMalloc of %zu B of workspace failed on device %d", bytes, dev);
+        if (hipMemsetAsync(p, 0, bytes, static_cast<hipStream_t>(stream)) != hipSuccess) {
+            (void)hipFree(p);
+            return fail(FA_ERR_WORKSPACE, "zeroing the workspace failed on device %d", dev);
+        }
+        if (!blk) {
+            g_ws.push_back({dev, stream, nullptr, 0, 0});
+            blk = &g_ws.back();
+        }
+        blk->ptr = static_cast<char*>(p);
+        blk->cap_items = cap_items;
+        blk->cap_parts = cap_parts;
+    }
+    ws->ctr = reinterpret_cast<int*>(blk->ptr);
+    ws->lw = reinterpret_cast<float*>(blk->ptr + workspace_lw_offset(blk->cap_items));
+    ws->o = reinterpret_cast<float*>(blk->ptr + workspace_o_offset(blk->cap_items, blk->cap_parts));
+    return FA_OK;
 }
 
 }  // namespace
 }  // namespace fa
 
-extern "C" int fa_prefill(const void* q, const void* k, const void* v, float* out, int n_q_heads,
-                          int n_kv_heads, int seq_len, int head_dim, float scale, int causal,
-                          void* stream) {
-    using namespace fa;
+namespace fa {
+namespace {
+
+// Both entry points: q_len queries at the last q_len of kv_len positions.
+int launch(const void* q, const void* k, const void* v, float* out, int n_q_heads, int n_kv_heads,
+           int q_len, int kv_len, int head_dim, float scale, int causal, void* stream) {
     clear_error();
     fa_plan plan;
-    int st = make_plan(n_q_heads, n_kv_heads, seq_len, head_dim, causal, 0, &plan);
+    int st = make_plan(n_q_heads, n_kv_heads, q_len, kv_len, head_dim, causal, 0, 0, nullptr);
     if (st != FA_OK) return st;
-    st = validate_call(q, k, v, out, n_q_heads, n_kv_heads, seq_len, head_dim, scale);
+    st = validate_call(q, k, v, out, n_q_heads, n_kv_heads, q_len, kv_len, head_dim, scale);
     if (st != FA_OK) return st;
-    if (seq_len == 0) return FA_OK;
+    if (q_len == 0) return FA_OK;
 
-    int dev = -1;
+    int dev = -1, n_cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(FA_ERR_DEVICE, "hipGetDevice failed");
-    st = check_device(dev);
+    st = check_device(dev, &n_cus);
     if (st != FA_OK) return st;
+    st = make_plan(n_q_heads, n_kv_heads, q_len, kv_len, head_dim, causal, 0, n_cus, &plan);
+    if (st != FA_OK) return st;
+    Workspace ws{nullptr, nullptr, nullptr};
+    int n_splits = plan.kv_splits;
+    if (n_splits > 1) {
+        const long long items = (long long)plan.n_q_tiles * n_q_heads;
+        st = acquire_workspace(dev, stream, items, items * n_splits, &ws);
+        if (st != FA_OK) return st;
+    }
 
     // Base-2 softmax: fold log2(e) into the scale.  A negative scale is
     // applied as |scale| with Q negated (exact in f16), so the kernel's
@@ -513,11 +725,47 @@ extern "C" int fa_prefill(const void* q, const void* k, const void* v, float* ou
     const _Float16* kh = static_cast<const _Float16*>(k);
     const _Float16* vh = static_cast<const _Float16*>(v);
     int n_q_tiles = plan.n_q_tiles;
-    void* args[] = {&qh, &kh, &vh, &out, &seq_len, &n_q_heads, &n_kv_heads, &n_q_tiles, &c2, &q_mode};
+    void* args[] = {&qh,    &kh,      &vh,     &out,    &q_len,  &kv_len,  &n_q_heads, &n_kv_heads,
+                    &n_q_tiles, &c2, &q_mode, &n_splits, &ws.ctr, &ws.lw, &ws.o};
     const void* fn = causal ? reinterpret_cast<const void*>(&fa_prefill_kernel<true>)
                             : reinterpret_cast<const void*>(&fa_prefill_kernel<false>);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)plan.n_groups), dim3(kThreads), args, 0,
                                    static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "hipLaunchKernel: %s", hipGetErrorString(e));
     return FA_OK;
+}
+
+}  // namespace
+}  // namespace fa
+
+extern "C" int fa_prefill(const void* q, const void* k, const void* v, float* out, int n_q_heads,
+                          int n_kv_heads, int seq_len, int head_dim, float scale, int causal,
+                          void* stream) {
+    return fa::launch(q, k, v, out, n_q_heads, n_kv_heads, seq_len, seq_len, head_dim, scale, causal,
+                      stream);
+}
+
+extern "C" int fa_prefill_free_workspaces(void) {
+    using namespace fa;
+    clear_error();
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    int st = FA_OK;
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    for (WorkspaceBlock& w : g_ws) {
+        // The stream may be gone; wait for the whole device instead.
+        if (hipSetDevice(w.dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+            hipFree(w.ptr) != hipSuccess)
+            st = fail(FA_ERR_WORKSPACE, "could not release the workspace of device %d", w.dev);
+    }
+    g_ws.clear();
+    if (prev >= 0) (void)hipSetDevice(prev);
+    return st;
+}
+
+extern "C" int fa_prefill_chunk(const void* q, const void* k, const void* v, float* out,
+                                int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim,
+                                float scale, int causal, void* stream) {
+    return fa::launch(q, k, v, out, n_q_heads, n_kv_heads, q_len, kv_len, head_dim, scale, causal,
+                      stream);
 }

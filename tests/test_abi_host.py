@@ -89,13 +89,17 @@ def test_seq_len_zero_is_ok_without_gpu():
 def test_plan_geometry(S, nq, nkv, causal):
     p = fa.fa_prefill_plan(nq, nkv, S, 128, causal)
     # the LDS request is exactly the sum of the planes the kernel lays out
-    assert p.lds_bytes == p.lds_k_bytes + p.lds_v_bytes
-    assert p.lds_k_bytes == p.kv_splits * p.stages * p.kv_tile * 128 * 2
-    assert p.lds_v_bytes == p.kv_splits * p.stages * p.kv_tile * 128 * 2
+    # (K and V stages, and a 16-byte merge flag)
+    assert p.lds_bytes == p.lds_k_bytes + p.lds_v_bytes + 16
+    assert p.lds_k_bytes == p.stages * p.kv_tile * 128 * 2
+    assert p.lds_v_bytes == p.stages * p.kv_tile * 128 * 2
     assert p.lds_bytes * (8 // p.waves_per_group) <= 160 * 1024  # 8 resident waves per CU fit 160 KiB
     assert p.threads_per_group == 64 * p.waves_per_group
-    assert p.q_tile * p.kv_splits == 32 * p.waves_per_group
+    assert p.q_tile == 32 * p.waves_per_group
     assert p.n_q_tiles == math.ceil(S / p.q_tile)
+    # a whole-sequence prefill is never split (its first query tile has no
+    # keys in front of it) and needs no workspace
+    assert p.kv_splits == 1 and p.workspace_bytes == 0
     assert p.n_groups == p.n_q_tiles * nq
     # KV tiles visited: causal groups stop at their last query row
     tiles = 0
@@ -121,3 +125,76 @@ def test_binding_rejects_bad_tensors_without_gpu():
         fa.attention(q, q, q, 0.1)  # CPU tensors are refused, never computed
     with pytest.raises(TypeError):
         fa.attention(q.float(), q, q, 0.1)
+
+
+# ------------------------------------------------------------ chunked prefill
+def call_chunk(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, out=FAKE + 0x400000, n_q_heads=4,
+             n_kv_heads=2, q_len=16, kv_len=48, head_dim=128, scale=0.088, causal=1, stream=None)
+    a.update(kw)
+    return fa.fa_prefill_chunk(a["q"], a["k"], a["v"], a["out"], a["n_q_heads"], a["n_kv_heads"],
+                               a["q_len"], a["kv_len"], a["head_dim"], a["scale"], a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(out=None), 1),
+    (dict(q_len=-1), 2), (dict(kv_len=15), 2), (dict(q_len=16, kv_len=-1), 2),
+    (dict(n_q_heads=6, n_kv_heads=4), 2), (dict(head_dim=64), 3), (dict(scale=float("nan")), 4),
+    (dict(k=FAKE + 0x100004), 5),
+    # out overlaps k, which is longer than q: [k, k + 48*2*256) covers k + 0x4000
+    (dict(out=FAKE + 0x100000 + 0x4000), 8),
+])
+def test_chunk_argument_errors(kw, code):
+    st = call_chunk(**kw)
+    assert st == code, (kw, st, fa.fa_prefill_last_error())
+
+
+def test_chunk_zero_queries_is_ok_without_gpu():
+    assert call_chunk(q_len=0, q=None, k=None, v=None, out=None) == 0
+
+
+@pytest.mark.parametrize("q_len,kv_len,causal", [
+    (512, 4096, 1), (1, 4096, 1), (129, 700, 1), (129, 700, 0), (2659, 2659, 1), (0, 100, 1),
+])
+def test_chunk_plan_geometry(q_len, kv_len, causal):
+    nq = 32
+    p = fa.fa_prefill_chunk_plan(nq, 8, q_len, kv_len, 128, causal)
+    assert p.n_q_tiles == math.ceil(q_len / p.q_tile)
+    assert p.n_groups == p.n_q_tiles * nq * p.kv_splits
+    off = kv_len - q_len
+    tiles = 0
+    for t in range(p.n_q_tiles):
+        kv_end = min(kv_len, off + (t + 1) * p.q_tile) if causal else kv_len
+        tiles += math.ceil(kv_end / p.kv_tile)
+    assert p.kv_tiles_visited == tiles * nq
+
+
+def workspace_bytes(items, parts, q_tile=128):
+    """Counters (rounded to 256 B), then per part q_tile log-weights and [q_tile][128] outputs."""
+    return -(-items * 4 // 256) * 256 + parts * q_tile * 4 + parts * q_tile * 128 * 4
+
+
+@pytest.mark.parametrize("nq,q_len,kv_len,causal,splits", [
+    (32, 512, 4096, 1, 4),    # 128 tiles on 512 slots, 56 shared key tiles: 4 parts
+    (32, 1, 4096, 1, 8),      # one new token: capped at 8 parts
+    (32, 1, 200, 1, 1),       # cache too short for parts of >= 4 key tiles
+    (32, 2048, 4096, 1, 1),   # 512 tiles already fill the slots
+    (8, 256, 8192, 0, 8),     # non-causal: every key is shared
+    (6, 1, 4096, 1, 1),       # head count not a multiple of 8: never split
+])
+def test_chunk_plan_splits(nq, q_len, kv_len, causal, splits):
+    p = fa.fa_prefill_chunk_plan(nq, nq // 2 if nq % 2 == 0 else nq, q_len, kv_len, 128, causal)
+    assert p.kv_splits == splits
+    items = p.n_q_tiles * nq
+    assert p.n_groups == items * splits
+    assert p.workspace_bytes == (workspace_bytes(items, items * splits) if splits > 1 else 0)
+
+
+def test_free_workspaces_without_any_is_ok():
+    fa.fa_prefill_free_workspaces()
+
+
+def test_chunk_plan_with_whole_sequence_equals_prefill_plan():
+    a = fa.fa_prefill_chunk_plan(32, 32, 2659, 2659, 128, 1).as_dict()
+    b = fa.fa_prefill_plan(32, 32, 2659, 128, 1).as_dict()
+    assert a == b

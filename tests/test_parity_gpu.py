@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_f64, parity_errors, within_tolerance
+from oracle import attention_chunk_f64, attention_f64, parity_errors, within_tolerance
 from oracle.attention import attention_rows_blocked
 from prefill_attention_amd.workloads import SCALE, WORKLOADS, make_custom_inputs, make_inputs, row_subset
 
@@ -215,3 +215,144 @@ def test_error_paths_on_device(fa):
     st = fa.fa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), 2, 2, 64, 128,
                        float("nan"), 1, None)
     assert st == 4
+
+
+# ---------------------------------------------------------------- chunked prefill
+# q_len new tokens at positions kv_len - q_len .. kv_len - 1 over a KV cache of
+# kv_len tokens (fa_prefill_chunk), against the oracle's attention_chunk_f64.
+
+def _run_chunk(fa, q, k, v, scale=SCALE, causal=True):
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    out = fa.attention(dq, dk, dv, scale, causal)  # q shorter than k/v: the chunk entry point
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def test_chunk_workload_full_parity(fa):
+    wl = WORKLOADS["chunk_512_4k"]
+    q, k, v = make_inputs(wl)
+    got = _run_chunk(fa, q, k, v)
+    ref = attention_chunk_f64(q, k, v, SCALE, True)
+    err = parity_errors(got, ref)
+    _report("chunk_512_4k", err)
+    assert within_tolerance(err), err
+
+
+@pytest.mark.parametrize("q_len,kv_len,heads", [
+    (1, 1, (2, 2)), (1, 77, (2, 1)), (1, 4096, (4, 2)),          # one new token (decode-like)
+    (5, 300, (3, 3)), (63, 64, (2, 1)), (64, 65, (2, 2)),
+    (127, 1000, (4, 4)), (128, 129, (2, 1)), (129, 700, (8, 2)),
+    (300, 301, (2, 2)), (257, 2049, (4, 1)), (640, 640, (2, 2)),
+])
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunk_shapes(fa, q_len, kv_len, heads, causal):
+    nq, nkv = heads
+    q, k, v = make_custom_inputs(kv_len, nq, nkv, seed=q_len * 7 + kv_len, q_len=q_len)
+    got = _run_chunk(fa, q, k, v, causal=causal)
+    ref = attention_chunk_f64(q, k, v, SCALE, causal)
+    err = parity_errors(got, ref)
+    assert within_tolerance(err), (q_len, kv_len, heads, causal, err)
+
+
+def test_chunk_is_bitwise_slice_of_full_prefill(fa):
+    # with a cache length that is a multiple of the 128-row query tile, a chunk
+    # groups its rows exactly as the whole prefill does: identical results
+    S, Q = 1536, 512
+    q, k, v = make_custom_inputs(S, 4, 2, seed=88)
+    full = _run(fa, q, k, v)
+    part = _run_chunk(fa, q[S - Q:].contiguous(), k, v)
+    assert np.array_equal(part, full[S - Q:])
+
+
+def test_chunk_other_scales_and_q0(fa):
+    q, k, v = make_custom_inputs(500, 2, 1, seed=89, q_len=200)
+    for scale in (0.0, -SCALE, 0.5):
+        err = parity_errors(_run_chunk(fa, q, k, v, scale=scale), attention_chunk_f64(q, k, v, scale, True))
+        assert within_tolerance(err), (scale, err)
+
+
+def test_chunk_error_paths_on_device(fa):
+    q, k, v = (t.cuda() for t in make_custom_inputs(64, 2, 2, seed=90, q_len=32))
+    out = torch.empty(32, 2, 128, dtype=torch.float32, device="cuda")
+    # kv_len shorter than q_len
+    st = fa.fa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), 2, 2, 32, 16, 128,
+                             SCALE, 1, None)
+    assert st == 2
+    # q_len 0 is a no-op
+    st = fa.fa_prefill_chunk(None, None, None, None, 2, 2, 0, 64, 128, SCALE, 1, None)
+    assert st == 0
+
+
+# ---------------------------------------------------------------- split-KV
+# Grids that would leave slots idle (a short chunk over a long cache) split each
+# query tile's key range over several work-groups and merge their partial
+# softmax states.  Head counts here are multiples of 8, so the split path runs.
+
+def _chunk_plan(fa, nq, nkv, q_len, kv_len, causal=True):
+    return fa.fa_prefill_chunk_plan(nq, nkv, q_len, kv_len, 128, int(causal))
+
+
+@pytest.mark.parametrize("q_len,kv_len,heads,causal", [
+    (1, 4096, (8, 2), True), (1, 600, (8, 8), True), (3, 1000, (16, 4), True),
+    (37, 3000, (8, 8), True), (129, 2051, (8, 1), True), (200, 5000, (16, 4), True),
+    (64, 700, (8, 8), False), (1, 2049, (32, 8), False),
+])
+def test_split_kv_parity(fa, q_len, kv_len, heads, causal):
+    nq, nkv = heads
+    assert _chunk_plan(fa, nq, nkv, q_len, kv_len, causal).kv_splits > 1, "shape chosen to split"
+    q, k, v = make_custom_inputs(kv_len, nq, nkv, seed=q_len + 3 * kv_len, q_len=q_len)
+    got = _run_chunk(fa, q, k, v, causal=causal)
+    ref = attention_chunk_f64(q, k, v, SCALE, causal)
+    err = parity_errors(got, ref)
+    _report(f"split q={q_len} kv={kv_len} heads={heads} causal={causal}", err)
+    assert within_tolerance(err), err
+
+
+def test_split_kv_deterministic_and_peaked(fa):
+    # parts whose softmax masses differ by many powers of two (keys of the
+    # newest quarter scaled up), merged in part order: identical on reruns
+    q_len, kv_len = 96, 4000
+    assert _chunk_plan(fa, 8, 2, q_len, kv_len).kv_splits > 1
+    q, k, v = make_custom_inputs(kv_len, 8, 2, seed=91, q_len=q_len)
+    k = k.clone()
+    k[3 * kv_len // 4:] = (k[3 * kv_len // 4:].float() * 5.0).half()
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    outs = [fa.attention(dq, dk, dv, SCALE, True) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(outs[0], o), "split-KV merge depends on arrival order"
+    err = parity_errors(outs[0].cpu().numpy().astype(np.float64), attention_chunk_f64(q, k, v, SCALE, True))
+    assert within_tolerance(err), err
+
+
+def test_split_kv_workspace_reuse_growth_and_streams(fa):
+    # shapes needing different workspace sizes, alternated on two streams
+    shapes = [(1, 2000, 8, 2), (128, 6000, 16, 4), (1, 2000, 8, 2), (40, 3000, 8, 8)]
+    cases = []
+    for i, (Q, S, nq, nkv) in enumerate(shapes):
+        assert _chunk_plan(fa, nq, nkv, Q, S).kv_splits > 1
+        q, k, v = make_custom_inputs(S, nq, nkv, seed=95 + i, q_len=Q)
+        cases.append((q, k, v, q.cuda(), k.cuda(), v.cuda()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(2):
+        for i, (_, _, _, dq, dk, dv) in enumerate(cases):
+            s = streams[(i + rep) % 2]
+            with torch.cuda.stream(s):
+                outs.append((i, fa.attention(dq, dk, dv, SCALE, True, stream=s)))
+    torch.cuda.synchronize()
+    first = {}
+    for i, o in outs:
+        if i in first:
+            assert torch.equal(first[i], o), f"shape {shapes[i]} differs between runs"
+        else:
+            first[i] = o
+    for i, (q, k, v, *_rest) in enumerate(cases):
+        err = parity_errors(first[i].cpu().numpy().astype(np.float64), attention_chunk_f64(q, k, v, SCALE, True))
+        assert within_tolerance(err), (shapes[i], err)
+    fa.fa_prefill_free_workspaces()
+    q, k, v, dq, dk, dv = cases[0]
+    again = fa.attention(dq, dk, dv, SCALE, True)   # allocates again after the release
+    torch.cuda.synchronize()
+    assert torch.equal(again, first[0])
