@@ -102,6 +102,10 @@ WORKLOADS = {
         "chunk_512_4k", "7B-layer chunked causal prefill: 512 new tokens over a 3584-token KV cache, "
         "32/32 heads, hd=128", 32, 32, 4096, seed=6, q_rows=512,
     ),
+    "chunk_16_8k": Workload(
+        "chunk_16_8k", "7B-layer chunked causal prefill: 16 new tokens over an 8176-token KV cache, "
+        "32/32 heads, hd=128", 32, 32, 8192, seed=7, q_rows=16,
+    ),
 }
 
 # Workload the throughput figure is quoted on.
