@@ -1,4 +1,4 @@
-"""CPU float64 oracle for causal prefill attention.
+"""CPU oracle for causal prefill attention (float64) and its K/V producer.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
 its Python binding) imports, links or calls this package.  Only ``tests/``,
@@ -20,6 +20,7 @@ from .attention import (
     softmax_rows,
     combine_values,
 )
+from .kv_store import convert_f16, decode_f16_bits, round_to_f16_bits, store_kv, store_rows
 from .compare import ATOL, RTOL, REL_FLOOR, parity_errors, within_tolerance
 
 __all__ = [
@@ -31,6 +32,11 @@ __all__ = [
     "visible_mask",
     "softmax_rows",
     "combine_values",
+    "convert_f16",
+    "decode_f16_bits",
+    "round_to_f16_bits",
+    "store_kv",
+    "store_rows",
     "ATOL",
     "RTOL",
     "REL_FLOOR",
