@@ -8,6 +8,11 @@ tokens x head_dim 128, causal, f16 in, f32 out by default), inputs resident in
 HBM.  W untimed steps, then K steps back to back on one stream, bracketed by
 HIP events and device synchronisation.  Prints one JSON line.
 
+A K/V producer workload (--workload kv_store_2659 etc.) times fa_store_kv
+instead: one step = one launch storing the workload's K and V, rotating over
+enough input/output sets that each launch streams from HBM; the figure is
+algorithmic bytes (f32 read, f16 written, positions read) per second.
+
 The reported throughput counts algorithmic FLOP only: 4 * head_dim per
 visible (query, key) pair per query head (Q.K^T and P.V multiply-adds, x2),
 not the masked upper triangle nor the padding of diagonal and tail tiles.
@@ -29,29 +34,35 @@ sys.path.insert(0, ROOT)
 PEAK_F16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("prefill_attention_amd/csrc/fa_prefill.hip", "prefill_attention_amd/csrc/fa_geometry.h")
+STORE_SOURCES = ("prefill_attention_amd/csrc/fa_kv_store.hip",)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_prefill_kernel_traffic.json")
+STORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_store_kv_traffic.json")
+# The producer's timed loop rotates over input/output sets whose total exceeds
+# this many bytes, so every launch streams from HBM rather than from the
+# 256 MB Infinity Cache (MALL) that a repeated 130 MB working set would hit.
+STORE_ROTATION_BYTES = 1 << 30
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_key: str):
+def measured_traffic(workload_key: str, path: str = TRAFFIC_FILE, sources=KERNEL_SOURCES):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None.
 
     Valid only for the kernel source they were taken on (hash recorded with
     the numbers) and for the same workload.
     """
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("workload") != workload_key:
+    if rec.get("kernel_source_hash") != kernel_source_hash(sources) or rec.get("workload") != workload_key:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -95,6 +106,104 @@ def cpu_baseline(wl, q, k, v, gpu_out, scale, budget_s: float = 12.0) -> dict:
     }
 
 
+def store_cpu_baseline(swl, k, v, pos, budget_s: float = 15.0) -> dict:
+    """Time the oracle's K/V store (numpy) on whole tokens of the workload."""
+    import numpy as np
+    from oracle import store_kv
+
+    cache = np.zeros((swl.cache_len, swl.n_kv_heads, swl.head_dim), dtype=np.uint16)
+    kn, vn, pn = k.numpy(), v.numpy(), pos.numpy()
+    done, t_used, chunk = 0, 0.0, max(1, min(swl.n_tokens, 256))
+    while done < swl.n_tokens and t_used < budget_s:
+        n = min(chunk, swl.n_tokens - done)
+        t0 = time.perf_counter()
+        store_kv(kn[done:done + n], vn[done:done + n], pn[done:done + n], cache, cache)
+        t_used += time.perf_counter() - t0
+        done += n
+    nbytes = 2 * done * swl.row * 6 + 4 * done
+    return {
+        "value": nbytes / t_used / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {done} of {swl.n_tokens} tokens, K and V ({nbytes / 1e6:.1f} MB algorithmic) "
+                  f"in {t_used:.1f} s; numpy, rounding by table search",
+        "seconds": round(t_used, 3),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def store_bench(args, key) -> int:
+    """Bench of the K/V producer (fa_store_kv): GB/s of algorithmic bytes."""
+    import torch
+
+    import prefill_attention_amd as fa
+    from prefill_attention_amd.workloads import STORE_WORKLOADS, make_store_inputs
+
+    swl = STORE_WORKLOADS[key]
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    k, v, pos = make_store_inputs(swl)
+    per_set = 2 * k.numel() * 4 + 2 * swl.cache_len * swl.row * 2 + pos.numel() * 4
+    n_sets = max(2, min(32, -(-STORE_ROTATION_BYTES // per_set)))
+    sets = []
+    for _ in range(n_sets):
+        kc = torch.zeros(swl.cache_len, swl.n_kv_heads, swl.head_dim, dtype=torch.float16, device=dev)
+        sets.append((k.to(dev), v.to(dev), pos.to(dev), kc, torch.zeros_like(kc)))
+    stream = torch.cuda.Stream(device=dev)
+    calls = [(a.data_ptr(), b.data_ptr(), p.data_ptr(), swl.n_tokens, swl.n_kv_heads, swl.head_dim,
+              c.data_ptr(), d.data_ptr(), swl.cache_len, None, stream.cuda_stream)
+             for a, b, p, c, d in sets]
+    fa.store_kv(*sets[0][:5], stream=stream)  # checked call first
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            fa.fa_store_kv(*calls[i % n_sets])
+        stream.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        statuses = [fa.fa_store_kv(*calls[i % n_sets]) for i in range(args.steps)]
+        end.record(stream)
+        end.synchronize()
+        torch.cuda.synchronize()
+    if any(statuses):
+        print(f"bench.py: fa_store_kv returned {set(statuses)}", file=sys.stderr)
+        return 1
+    ms_per_step = start.elapsed_time(end) / args.steps
+    gbs = swl.algorithmic_bytes / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": f"K/V store GB/s, algorithmic bytes ({swl.name})",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32->f16",
+        "data": "synthetic",
+        "config": {**swl.describe(), "workload_key": key, "rotating_sets": n_sets},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(key, STORE_TRAFFIC_FILE, STORE_SOURCES),
+            "bytes_per_launch": swl.algorithmic_bytes,
+            "avg_launch_us": round(ms_per_step * 1e3, 3),
+            "kernel_source_hash": kernel_source_hash(STORE_SOURCES),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = store_cpu_baseline(swl, k, v, pos)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,7 +243,15 @@ def main() -> int:
         print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
                           "launches": args.steps}), flush=True)
         return 0
+    from prefill_attention_amd.workloads import STORE_WORKLOADS
+
     key = args.workload or HEADLINE
+    if key in STORE_WORKLOADS:
+        return store_bench(args, key)
+    if key not in WORKLOADS:
+        print(f"bench.py: unknown workload {key!r}; known: {sorted(WORKLOADS) + sorted(STORE_WORKLOADS)}",
+              file=sys.stderr)
+        return 2
     wl = WORKLOADS[key]
     fa.load_library()
     dev = torch.device("cuda:0")

@@ -27,9 +27,10 @@ STATUS_NAMES = {
     9: "FA_ERR_DEVICE",
     10: "FA_ERR_WORKSPACE",
 }
-# Every symbol include/fa_prefill.h declares.
+# Every symbol include/fa_prefill.h and include/fa_kv_store.h declare.
 EXPORTED = ("fa_prefill", "fa_prefill_chunk", "fa_prefill_plan", "fa_prefill_chunk_plan",
-            "fa_prefill_free_workspaces", "fa_prefill_strerror", "fa_prefill_last_error")
+            "fa_prefill_free_workspaces", "fa_prefill_strerror", "fa_prefill_last_error",
+            "fa_store_kv", "fa_convert_f16")
 
 
 class FaPlan(ctypes.Structure):
@@ -105,6 +106,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_prefill_strerror.argtypes = [ctypes.c_int]
         lib.fa_prefill_last_error.restype = ctypes.c_char_p
         lib.fa_prefill_last_error.argtypes = []
+        lib.fa_store_kv.restype = ctypes.c_int
+        lib.fa_store_kv.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_void_p,
+        ]
+        lib.fa_convert_f16.restype = ctypes.c_int
+        lib.fa_convert_f16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong,
+                                       ctypes.c_void_p]
         _lib = lib
         return lib
 
@@ -205,5 +215,81 @@ def attention(q, k, v, scale: float, causal: bool = True, out=None, stream=None)
         else:
             status = fa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), n_q,
                                       k.shape[1], Q, S, hd, scale, 1 if causal else 0, handle)
+    _check(status)
+    return out
+
+
+def fa_store_kv(k_new, v_new, positions, n_tokens: int, n_kv_heads: int, head_dim: int, k_cache,
+                v_cache, cache_len: int, n_skipped, stream) -> int:
+    """Same arguments as the C function; pointers as ints (or None), returns the status."""
+    lib = load_library()
+    return lib.fa_store_kv(k_new, v_new, positions, int(n_tokens), int(n_kv_heads), int(head_dim),
+                           k_cache, v_cache, int(cache_len), n_skipped, stream)
+
+
+def fa_convert_f16(x, y, n: int, stream) -> int:
+    """Same arguments as the C function; pointers as ints (or None), returns the status."""
+    return load_library().fa_convert_f16(x, y, int(n), stream)
+
+
+def _stream_handle(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def store_kv(k_new, v_new, positions, k_cache, v_cache, n_skipped=None, stream=None):
+    """Torch-facing K/V store: f32 [T, Hkv, D] rows -> f16 cache rows positions[t].
+
+    k_new, v_new: contiguous float32 [T, n_kv_heads, head_dim]; positions:
+    int32 [T]; k_cache, v_cache: contiguous float16 [cache_len, n_kv_heads,
+    head_dim]; n_skipped: optional int32 [1] counter (see fa_kv_store.h).  All
+    on one GPU.  Enqueues one kernel and returns (k_cache, v_cache).
+    """
+    import torch
+
+    for name, t, dt in (("k_new", k_new, torch.float32), ("v_new", v_new, torch.float32),
+                        ("positions", positions, torch.int32), ("k_cache", k_cache, torch.float16),
+                        ("v_cache", v_cache, torch.float16)):
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_cuda or t.device != k_new.device:
+            raise ValueError(f"{name} must be on k_new's GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k_new.dim() != 3 or k_new.shape != v_new.shape or k_cache.shape != v_cache.shape \
+            or k_cache.dim() != 3 or k_cache.shape[1:] != k_new.shape[1:]:
+        raise ValueError("k_new/v_new [T, H, D] and k_cache/v_cache [cache_len, H, D] must agree")
+    if positions.shape != (k_new.shape[0],):
+        raise ValueError("positions must be int32 [T]")
+    cnt = 0
+    if n_skipped is not None:
+        if n_skipped.dtype != torch.int32 or not n_skipped.is_cuda or n_skipped.numel() < 1:
+            raise ValueError("n_skipped must be an int32 GPU tensor")
+        cnt = n_skipped.data_ptr()
+    T, H, D = k_new.shape
+    with torch.cuda.device(k_new.device):
+        status = fa_store_kv(k_new.data_ptr(), v_new.data_ptr(), positions.data_ptr(), T, H, D,
+                             k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[0], cnt or None,
+                             _stream_handle(stream, k_new.device))
+    _check(status)
+    return k_cache, v_cache
+
+
+def convert_f16(x, out=None, stream=None):
+    """Torch-facing f32 -> f16 conversion of a contiguous GPU tensor (same shape)."""
+    import torch
+
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 GPU tensor")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float16, device=x.device)
+    elif out.dtype != torch.float16 or out.shape != x.shape or not out.is_contiguous() \
+            or out.device != x.device:
+        raise ValueError("out must be a contiguous float16 tensor shaped like x on x's device")
+    with torch.cuda.device(x.device):
+        status = fa_convert_f16(x.data_ptr(), out.data_ptr(), x.numel(), _stream_handle(stream, x.device))
     _check(status)
     return out

@@ -2,8 +2,8 @@
 
     python -m prefill_attention_amd.build        # or __graft_entry__.build()
 
-The HIP translation unit is compiled for gfx950 only; the planner is plain
-C++.  Packed-FP32 VALU forms are disabled for the device code.
+The HIP translation units (attention, K/V producer) are compiled for
+gfx950 only; the planner is plain C++.  Packed-FP32 VALU forms are disabled for the device code.
 """
 
 from __future__ import annotations
@@ -54,8 +54,10 @@ def build(verbose_resources: bool = False) -> str:
     if verbose_resources:
         dev_flags += ["-Rpass-analysis=kernel-resource-usage"]
     _run([hipcc, *common, *dev_flags, "-c", os.path.join(CSRC, "fa_prefill.hip"), "-o", kern_o])
+    store_o = os.path.join(BUILD_DIR, "fa_kv_store.o")
+    _run([hipcc, *common, *dev_flags, "-c", os.path.join(CSRC, "fa_kv_store.hip"), "-o", store_o])
     tmp = LIB_PATH + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", plan_o, kern_o, "-o", tmp])
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", plan_o, kern_o, store_o, "-o", tmp])
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -1,5 +1,5 @@
-// Internal declarations shared by the planner (fa_plan.cpp) and the launcher
-// (fa_prefill.hip).
+// Internal declarations shared by the planner (fa_plan.cpp), the attention
+// launcher (fa_prefill.hip) and the K/V producer (fa_kv_store.hip).
 #pragma once
 
 #include "fa_prefill.h"
@@ -24,6 +24,16 @@ int make_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim
 long long workspace_lw_offset(long long cap_items);
 long long workspace_o_offset(long long cap_items, long long cap_parts);
 long long workspace_bytes(long long cap_items, long long cap_parts);
+
+// The current HIP device is usable by this library (gfx950, enough LDS);
+// the result is cached per device, with its compute-unit count.
+int check_device(int dev, int* n_cus);
+
+// Argument checks of the K/V producer's entry points (host only).
+int validate_store_kv(const float* k_new, const float* v_new, const int* positions, int n_tokens,
+                      int n_kv_heads, int head_dim, const void* k_cache, const void* v_cache,
+                      int cache_len, const int* n_skipped);
+int validate_convert(const float* x, const void* y, long long n);
 
 // Pointer, alignment, aliasing and scale checks of one call.
 int validate_call(const void* q, const void* k, const void* v, const float* out, int n_q_heads,

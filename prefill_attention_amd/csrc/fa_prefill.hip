@@ -596,11 +596,16 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     }
 }
 
+}  // namespace
+
 // Per-device check: gfx950 and the LDS limit, cached (0 unknown, 1 ok, else
 // the error), with the device's compute-unit count.
+namespace {
 constexpr int kMaxDevices = 64;
 int g_device_state[kMaxDevices];
 int g_device_cus[kMaxDevices];
+
+}  // namespace
 
 int check_device(int dev, int* n_cus) {
     if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_DEVICE, "device index %d out of range", dev);
@@ -625,6 +630,8 @@ int check_device(int dev, int* n_cus) {
     *n_cus = prop.multiProcessorCount;
     return result;
 }
+
+namespace {
 
 // Library-owned workspace blocks, one per (device, stream).  A block only
 // grows; it is zeroed when allocated and every kernel leaves its arrival

@@ -19,6 +19,11 @@ drawn in that order, S = ``seq_len`` keys and Q = ``q_len`` queries.  A
 full prefill has Q = S.  A chunked prefill (Q < S) is the last Q tokens of
 an S-token sequence whose first S - Q tokens are already in the KV cache: its
 queries sit at positions S - Q .. S - 1.  scale = float32(1 / sqrt(128)).
+
+The K/V producer's workloads (``STORE_WORKLOADS``) draw f32 K and V rows
+from N(0, 1), the activations the attention inputs above are rounded from,
+at the same head counts, with the appended or scattered cache positions
+described in ``StoreWorkload``.
 """
 
 from __future__ import annotations
@@ -132,6 +137,91 @@ def make_custom_inputs(seq_len: int, n_q_heads: int, n_kv_heads: int, seed: int,
     wl = Workload("custom", "custom", n_q_heads, n_kv_heads, seq_len, seed, k_mult=k_mult, head_dim=head_dim,
                   q_rows=q_len)
     return make_inputs(wl)
+
+
+def make_kv_f32(wl: Workload, seed: int | None = None):
+    """(k, v) float32 [seq_len, n_kv_heads, hd]: the draws of ``make_inputs``
+    before their rounding to f16 (same generator, same order, q drawn and
+    discarded first)."""
+    g = torch.Generator(device="cpu").manual_seed(wl.seed if seed is None else seed)
+    S, hd = wl.seq_len, wl.head_dim
+    torch.randn([wl.q_len, wl.n_q_heads, hd], dtype=torch.float32, generator=g)
+    k = wl.k_mult * torch.randn([S, wl.n_kv_heads, hd], dtype=torch.float32, generator=g)
+    v = torch.randn([S, wl.n_kv_heads, hd], dtype=torch.float32, generator=g)
+    return k, v
+
+
+# ------------------------------------------------------------ K/V producer
+@dataclass(frozen=True)
+class StoreWorkload:
+    """One call of the K/V producer: n_tokens f32 K/V rows stored as f16 at
+    their positions in a cache of cache_len rows.
+
+    Positions are the last n_tokens rows of the cache in order (a prompt or a
+    chunk appended to what the cache holds), or, with ``scatter``, n_tokens
+    distinct rows drawn at random (the general form of the pages' positions
+    array, "11 · P5 — prefill gap session", §3.2).
+    """
+
+    key: str
+    name: str
+    n_tokens: int
+    n_kv_heads: int
+    cache_len: int
+    seed: int
+    head_dim: int = HEAD_DIM
+    scatter: bool = False
+
+    @property
+    def row(self) -> int:
+        return self.n_kv_heads * self.head_dim
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Bytes one call must move: K and V read as f32, written as f16, positions read."""
+        return 2 * self.n_tokens * self.row * (4 + 2) + 4 * self.n_tokens
+
+    def describe(self) -> dict:
+        return {
+            "workload": self.name,
+            "n_tokens": self.n_tokens,
+            "n_kv_heads": self.n_kv_heads,
+            "head_dim": self.head_dim,
+            "cache_len": self.cache_len,
+            "positions": "scattered" if self.scatter else "appended",
+            "dtype_in": "f32",
+            "dtype_out": "f16",
+        }
+
+
+STORE_WORKLOADS = {
+    "kv_store_2659": StoreWorkload(
+        "kv_store_2659", "K/V store of a 2659-token prompt, 32 kv heads, hd=128, into a 2659-row cache",
+        2659, 32, 2659, seed=21),
+    "kv_store_chunk_512_4k": StoreWorkload(
+        "kv_store_chunk_512_4k", "K/V store of a 512-token chunk at rows 3584..4095 of a 4096-row cache, "
+        "32 kv heads, hd=128", 512, 32, 4096, seed=22),
+    "kv_store_gqa_4k": StoreWorkload(
+        "kv_store_gqa_4k", "K/V store of a 4096-token prompt, 8 kv heads, hd=128, into a 4096-row cache",
+        4096, 8, 4096, seed=23),
+    "kv_store_scatter": StoreWorkload(
+        "kv_store_scatter", "K/V store of 1000 tokens at scattered rows of a 5000-row cache, 8 kv heads, "
+        "hd=128", 1000, 8, 5000, seed=24, scatter=True),
+}
+
+
+def make_store_inputs(swl: StoreWorkload, seed: int | None = None):
+    """(k_new, v_new, positions): float32 [n_tokens, n_kv_heads, hd] N(0, 1)
+    draws (K then V) and int32 [n_tokens] cache rows, from one CPU generator."""
+    g = torch.Generator(device="cpu").manual_seed(swl.seed if seed is None else seed)
+    shape = [swl.n_tokens, swl.n_kv_heads, swl.head_dim]
+    k = torch.randn(shape, dtype=torch.float32, generator=g)
+    v = torch.randn(shape, dtype=torch.float32, generator=g)
+    if swl.scatter:
+        pos = torch.randperm(swl.cache_len, generator=g)[: swl.n_tokens]
+    else:
+        pos = torch.arange(swl.cache_len - swl.n_tokens, swl.cache_len)
+    return k, v, pos.to(torch.int32)
 
 
 def row_subset(seq_len: int, n_rows: int, seed: int) -> np.ndarray:
