@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 # MI355X published dense f16 matrix peak: 256 CUs x 4096 FLOP/clk x 2.4 GHz.
 PEAK_F16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ("prefill_attention_amd/csrc/fa_prefill.hip", "prefill_attention_amd/csrc/fa_geometry.h")
+KERNEL_SOURCES = ("prefill_attention_amd/csrc/fa_prefill_kernel.h", "prefill_attention_amd/csrc/fa_prefill_hd128.hip",
+                  "prefill_attention_amd/csrc/fa_geometry.h")
 STORE_SOURCES = ("prefill_attention_amd/csrc/fa_kv_store.hip",)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_prefill_kernel_traffic.json")
 STORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_store_kv_traffic.json")
@@ -81,7 +82,7 @@ def cpu_baseline(wl, q, k, v, gpu_out, scale, budget_s: float = 12.0) -> dict:
         threads = len(os.sched_getaffinity(0))
     group = wl.n_q_heads // wl.n_kv_heads
     heads, t_used, worst = 0, 0.0, 0.0
-    gpu_np = gpu_out.cpu().numpy()
+    gpu_np = gpu_out.float().cpu().numpy()
     while heads < wl.n_q_heads and t_used < budget_s:
         h = heads
         hk = h // group
@@ -257,23 +258,36 @@ def main() -> int:
     dev = torch.device("cuda:0")
     q, k, v = make_inputs(wl)
     dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
-    out = torch.empty((wl.q_len, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    from prefill_attention_amd.binding import FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32
+    from prefill_attention_amd.workloads import TORCH_DTYPES
+
+    scale = wl.scale
+    out_dt = TORCH_DTYPES[wl.out_dtype]
+    out = torch.empty((wl.q_len, wl.n_q_heads, wl.head_dim), dtype=out_dt, device=dev)
     stream = torch.cuda.Stream(device=dev)
+    codes = {"f16": FA_DTYPE_F16, "bf16": FA_DTYPE_BF16, "f32": FA_DTYPE_F32}
     # One step = one call of the C entry point (argument marshalling done once,
     # so the timed loop is not bound by Python-side checks).
-    if wl.chunked:
+    if (wl.in_dtype, wl.out_dtype) != ("f16", "f32"):
+        plan = fa.fa_prefill_chunk_plan(wl.n_q_heads, wl.n_kv_heads, wl.q_len, wl.seq_len, wl.head_dim,
+                                        int(wl.causal))
+        entry = fa.fa_prefill_ex
+        call_args = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), wl.n_q_heads,
+                     wl.n_kv_heads, wl.q_len, wl.seq_len, wl.head_dim, scale, int(wl.causal),
+                     codes[wl.in_dtype], codes[wl.out_dtype], stream.cuda_stream)
+    elif wl.chunked:
         plan = fa.fa_prefill_chunk_plan(wl.n_q_heads, wl.n_kv_heads, wl.q_len, wl.seq_len, wl.head_dim,
                                         int(wl.causal))
         entry = fa.fa_prefill_chunk
         call_args = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), wl.n_q_heads,
-                     wl.n_kv_heads, wl.q_len, wl.seq_len, wl.head_dim, SCALE, int(wl.causal),
+                     wl.n_kv_heads, wl.q_len, wl.seq_len, wl.head_dim, scale, int(wl.causal),
                      stream.cuda_stream)
     else:
         plan = fa.fa_prefill_plan(wl.n_q_heads, wl.n_kv_heads, wl.seq_len, wl.head_dim, int(wl.causal))
         entry = fa.fa_prefill
         call_args = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), out.data_ptr(), wl.n_q_heads,
-                     wl.n_kv_heads, wl.seq_len, wl.head_dim, SCALE, int(wl.causal), stream.cuda_stream)
-    fa.attention(dq, dk, dv, SCALE, wl.causal, out=out, stream=stream)  # checked call first
+                     wl.n_kv_heads, wl.seq_len, wl.head_dim, scale, int(wl.causal), stream.cuda_stream)
+    fa.attention(dq, dk, dv, scale, wl.causal, out=out, stream=stream)  # checked call first
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -294,7 +308,7 @@ def main() -> int:
     tflops = wl.flop / (ms_per_step * 1e-3) / 1e12
 
     traffic = measured_traffic(key)
-    min_bytes = (q.numel() + k.numel() + v.numel()) * 2 + out.numel() * 4
+    min_bytes = (q.numel() + k.numel() + v.numel()) * 2 + out.numel() * out.element_size()
     line = {
         "metric": "causal FA prefill TFLOP/s + % f16 MFMA peak (S=2659, 32 heads, hd=128)"
         if key == HEADLINE else f"causal FA {'chunked ' if wl.chunked else ''}prefill TFLOP/s ({wl.name})",
@@ -307,11 +321,11 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": wl.in_dtype,
         "data": "synthetic",
         "config": {**wl.describe(), "workload_key": key, "plan": plan.as_dict()},
         "pct_peak": round(100.0 * tflops / PEAK_F16_TFLOPS, 2),
-        "peak_basis": "MI355X dense f16 MFMA 256 CU x 4096 FLOP/clk x 2.4 GHz = 2516.6 TFLOP/s",
+        "peak_basis": f"MI355X dense {wl.in_dtype} MFMA 256 CU x 4096 FLOP/clk x 2.4 GHz = 2516.6 TFLOP/s",
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),
@@ -326,7 +340,7 @@ def main() -> int:
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, q, k, v, out, SCALE)
+        line["cpu_baseline"] = cpu_baseline(wl, q, k, v, out, scale)
     print(json.dumps(line), flush=True)
     return 0
 

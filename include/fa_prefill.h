@@ -29,14 +29,19 @@
  *
  * Precision.  f16 inputs, f32 accumulation in the matrix cores, the softmax
  * in f32 registers, probabilities rounded to f16 (round to nearest even) as
- * the operand of P.V, f32 output.
+ * the operand of P.V, f32 output.  fa_prefill_ex also takes bf16 inputs
+ * (probabilities then rounded to bf16, the operand type of P.V) and an
+ * output in the input type (rounded to nearest even from the f32 result).
+ * The pages' model uses head_dim 128; 64 and 256 run the same kernel with
+ * narrower or wider rows.
  *
  * Layout.  All tensors are dense, token-major, row-major:
  *     q   f16 [seq_len][n_q_heads][head_dim]     (chunk: [q_len][...])
  *     k   f16 [seq_len][n_kv_heads][head_dim]    (chunk: [kv_len][...])
  *     v   f16 [seq_len][n_kv_heads][head_dim]    (chunk: [kv_len][...])
  *     out f32 [seq_len][n_q_heads][head_dim]     (chunk: [q_len][...])
- * (so one token's row of one head is head_dim contiguous elements).
+ * (so one token's row of one head is head_dim contiguous elements; with
+ * fa_prefill_ex the element types are in_dtype and out_dtype).
  *
  * Ownership.  q, k, v and out are device memory owned by the caller; the
  * library keeps no reference to them after the call returns.  out must not
@@ -76,18 +81,25 @@ typedef enum fa_status {
     FA_ERR_SHAPE = 2,     /* a length < 0, kv_len < q_len, heads <= 0,
                              n_q_heads % n_kv_heads != 0, or a size that overflows
                              the launch grid                                       */
-    FA_ERR_HEAD_DIM = 3,  /* head_dim != 128                                       */
+    FA_ERR_HEAD_DIM = 3,  /* head_dim not 64, 128 or 256                           */
     FA_ERR_SCALE = 4,     /* scale is NaN or infinite                              */
     FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                      */
     FA_ERR_RESOURCE = 6,  /* the launch plan exceeds a device limit (LDS bytes)     */
     FA_ERR_LAUNCH = 7,    /* the HIP runtime reported an error at launch           */
     FA_ERR_ALIAS = 8,     /* out overlaps q, k or v                                */
     FA_ERR_DEVICE = 9,    /* no usable device, or the device is not gfx950         */
-    FA_ERR_WORKSPACE = 10 /* the library could not allocate or release its workspace */
+    FA_ERR_WORKSPACE = 10, /* the library could not allocate or release its workspace */
+    FA_ERR_DTYPE = 11     /* an unsupported input or output element type (fa_prefill_ex) */
 } fa_status;
 
-/* The only head dimension the kernel is built for (the pages' model uses
- * head_dim 128 throughout). */
+/* Element types of fa_prefill_ex. */
+typedef enum fa_dtype {
+    FA_DTYPE_F16 = 0,     /* IEEE binary16                                          */
+    FA_DTYPE_BF16 = 1,    /* bfloat16 (8 exponent bits, 7 fraction bits)            */
+    FA_DTYPE_F32 = 2      /* IEEE binary32 (outputs only)                            */
+} fa_dtype;
+
+/* The pages' head dimension; 64 and 256 are also built. */
 #define FA_HEAD_DIM 128
 
 /* Launch plan of one fa_prefill call: pure host arithmetic, no GPU needed. */
@@ -103,10 +115,11 @@ typedef struct fa_plan {
     int stages;              /* K/V tiles resident in LDS                          */
     int lds_bytes;           /* LDS per work-group: the sum of its planes (K, V and
                                 a 16-byte flag)                                    */
-    int lds_k_bytes;         /* K planes: stages x [kv_tile][head_dim] f16         */
-    int lds_v_bytes;         /* V planes: stages x [kv_tile][head_dim] f16         */
+    int lds_k_bytes;         /* K planes: stages x [kv_tile][head_dim] 16-bit      */
+    int lds_v_bytes;         /* V planes: stages x [kv_tile][head_dim] 16-bit      */
     long long kv_tiles_visited; /* KV tiles the grid visits (causal tiles skipped) */
     long long workspace_bytes;  /* library-owned device scratch the call needs (0: none) */
+    int groups_per_cu;       /* work-groups resident per compute unit (2; 1 for head_dim 256) */
 } fa_plan;
 
 /*
@@ -116,7 +129,7 @@ typedef struct fa_plan {
  *   n_q_heads  >= 1, a multiple of n_kv_heads
  *   n_kv_heads >= 1
  *   seq_len    >= 0 (0: nothing is launched, FA_OK)
- *   head_dim   must be FA_HEAD_DIM
+ *   head_dim   64, 128 (the pages' value) or 256
  *   scale      finite; multiplies q.k (typically 1/sqrt(head_dim))
  *   causal     0: every key visible; nonzero: key j visible from query i iff j <= i
  *   stream     hipStream_t to enqueue on (NULL: the null stream)
@@ -140,6 +153,18 @@ int fa_prefill_chunk(const void* q, const void* k, const void* v, float* out,
                      float scale, int causal, void* stream);
 
 /*
+ * Enqueue chunked (q_len < kv_len) or whole (q_len == kv_len) prefill
+ * attention with chosen element types: fa_prefill_chunk's arguments, plus
+ *   in_dtype   FA_DTYPE_F16 or FA_DTYPE_BF16: the type of q, k and v
+ *   out_dtype  FA_DTYPE_F32 or in_dtype: the type of out
+ * out is [q_len][n_q_heads][head_dim] of out_dtype.  Other combinations are
+ * FA_ERR_DTYPE.  fa_prefill_chunk is the (FA_DTYPE_F16, FA_DTYPE_F32) case.
+ */
+int fa_prefill_ex(const void* q, const void* k, const void* v, void* out,
+                  int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim,
+                  float scale, int causal, int in_dtype, int out_dtype, void* stream);
+
+/*
  * Compute the launch plan fa_prefill would use, without touching the GPU, for
  * an MI355X (256 compute units; fa_prefill plans for the current device).
  * Validates the shape arguments exactly as fa_prefill does (pointers aside).
@@ -149,7 +174,8 @@ int fa_prefill_chunk(const void* q, const void* k, const void* v, float* out,
 int fa_prefill_plan(int n_q_heads, int n_kv_heads, int seq_len, int head_dim,
                     int causal, int max_lds_bytes, fa_plan* plan);
 
-/* The plan fa_prefill_chunk would use (same validation, no GPU). */
+/* The plan fa_prefill_chunk (or fa_prefill_ex, whose element types do not
+ * change the plan) would use (same validation, no GPU). */
 int fa_prefill_chunk_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim,
                           int causal, int max_lds_bytes, fa_plan* plan);
 

@@ -21,7 +21,7 @@ from .attention import (
     combine_values,
 )
 from .kv_store import convert_f16, decode_f16_bits, round_to_f16_bits, store_kv, store_rows
-from .compare import ATOL, RTOL, REL_FLOOR, parity_errors, within_tolerance
+from .compare import ATOL, BF16_FACTOR, OUT_UNIT, REL_FLOOR, RTOL, bar, parity_errors, within_tolerance
 
 __all__ = [
     "attention_chunk_f64",
@@ -38,6 +38,9 @@ __all__ = [
     "store_kv",
     "store_rows",
     "ATOL",
+    "BF16_FACTOR",
+    "OUT_UNIT",
+    "bar",
     "RTOL",
     "REL_FLOOR",
     "parity_errors",

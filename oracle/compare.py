@@ -19,9 +19,30 @@ ATOL = 2e-3
 RTOL = 1e-2
 REL_FLOOR = ATOL / RTOL  # 0.2
 
+# Other element types, derived from the f16 bar (see DESIGN):
+# * bf16 inputs: the probabilities enter P.V rounded to bf16, whose unit
+#   roundoff (2^-8) is 8 times f16's (2^-11); the error the bar allows for
+#   that rounding scales with it, so the bar is 8 x (ATOL, RTOL).
+# * a 16-bit output adds one rounding of the f32 result, at most half an
+#   ulp: |o| * OUT_UNIT[type]; parity_errors(out_unit=...) removes exactly
+#   that allowance before the bar is applied.
+BF16_FACTOR = 8.0
+OUT_UNIT = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
-def parity_errors(got, ref) -> dict:
-    """max_abs, max_rel (floored) and norm-wise error of ``got`` vs ``ref``."""
+
+def bar(in_dtype: str = "f16") -> tuple[float, float]:
+    """(atol, rtol) for the input type."""
+    f = BF16_FACTOR if in_dtype == "bf16" else 1.0
+    return ATOL * f, RTOL * f
+
+
+def parity_errors(got, ref, out_unit: float = 0.0) -> dict:
+    """max_abs, max_rel (floored) and norm-wise error of ``got`` vs ``ref``.
+
+    ``out_unit`` > 0: ``got`` was rounded to a 16-bit type with that unit
+    roundoff; each element's difference is first reduced by out_unit * |ref|
+    (the largest error the rounding alone can make).
+    """
     g = np.asarray(got, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
     if g.shape != r.shape:
@@ -29,7 +50,7 @@ def parity_errors(got, ref) -> dict:
     if g.size == 0:
         return {"max_abs": 0.0, "max_rel": 0.0, "normwise": 0.0, "finite": True}
     finite = bool(np.all(np.isfinite(g)))
-    d = np.abs(g - r)
+    d = np.maximum(np.abs(g - r) - out_unit * np.abs(r), 0.0)
     max_abs = float(np.max(d)) if finite else float("inf")
     max_rel = float(np.max(d / np.maximum(np.abs(r), REL_FLOOR))) if finite else float("inf")
     denom = float(np.max(np.abs(r)))

@@ -15,6 +15,7 @@ from .binding import (
     fa_prefill,
     fa_prefill_chunk,
     fa_prefill_chunk_plan,
+    fa_prefill_ex,
     fa_prefill_free_workspaces,
     fa_prefill_last_error,
     fa_prefill_plan,
@@ -34,6 +35,7 @@ __all__ = [
     "fa_prefill",
     "fa_prefill_chunk",
     "fa_prefill_chunk_plan",
+    "fa_prefill_ex",
     "fa_prefill_free_workspaces",
     "fa_prefill_last_error",
     "fa_prefill_plan",

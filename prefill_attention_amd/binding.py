@@ -26,9 +26,13 @@ STATUS_NAMES = {
     8: "FA_ERR_ALIAS",
     9: "FA_ERR_DEVICE",
     10: "FA_ERR_WORKSPACE",
+    11: "FA_ERR_DTYPE",
 }
+# fa_dtype codes
+FA_DTYPE_F16, FA_DTYPE_BF16, FA_DTYPE_F32 = 0, 1, 2
+HEAD_DIMS = (64, 128, 256)
 # Every symbol include/fa_prefill.h and include/fa_kv_store.h declare.
-EXPORTED = ("fa_prefill", "fa_prefill_chunk", "fa_prefill_plan", "fa_prefill_chunk_plan",
+EXPORTED = ("fa_prefill", "fa_prefill_chunk", "fa_prefill_ex", "fa_prefill_plan", "fa_prefill_chunk_plan",
             "fa_prefill_free_workspaces", "fa_prefill_strerror", "fa_prefill_last_error",
             "fa_store_kv", "fa_convert_f16")
 
@@ -50,6 +54,7 @@ class FaPlan(ctypes.Structure):
         ("lds_v_bytes", ctypes.c_int),
         ("kv_tiles_visited", ctypes.c_longlong),
         ("workspace_bytes", ctypes.c_longlong),
+        ("groups_per_cu", ctypes.c_int),
     ]
 
     def as_dict(self) -> dict:
@@ -89,6 +94,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p,
+        ]
+        lib.fa_prefill_ex.restype = ctypes.c_int
+        lib.fa_prefill_ex.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
         ]
         lib.fa_prefill_chunk_plan.restype = ctypes.c_int
         lib.fa_prefill_chunk_plan.argtypes = [
@@ -142,6 +153,14 @@ def fa_prefill_chunk(q, k, v, out, n_q_heads: int, n_kv_heads: int, q_len: int, 
                                 int(head_dim), float(scale), int(causal), stream)
 
 
+def fa_prefill_ex(q, k, v, out, n_q_heads: int, n_kv_heads: int, q_len: int, kv_len: int,
+                  head_dim: int, scale: float, causal: int, in_dtype: int, out_dtype: int, stream) -> int:
+    """Same arguments as the C function; pointers as ints (or None), returns the status."""
+    lib = load_library()
+    return lib.fa_prefill_ex(q, k, v, out, int(n_q_heads), int(n_kv_heads), int(q_len), int(kv_len),
+                             int(head_dim), float(scale), int(causal), int(in_dtype), int(out_dtype), stream)
+
+
 def fa_prefill_chunk_plan(n_q_heads: int, n_kv_heads: int, q_len: int, kv_len: int, head_dim: int,
                           causal: int, max_lds_bytes: int = 0) -> FaPlan:
     """Launch plan of a chunked call (no GPU); raises FaError on invalid shapes."""
@@ -175,25 +194,35 @@ def fa_prefill_last_error() -> str:
     return load_library().fa_prefill_last_error().decode()
 
 
-def attention(q, k, v, scale: float, causal: bool = True, out=None, stream=None):
-    """Torch-facing call: q [Q, Hq, 128] f16, k/v [S, Hkv, 128] f16 on one GPU.
+def attention(q, k, v, scale: float, causal: bool = True, out=None, stream=None, out_dtype=None):
+    """Torch-facing call: q [Q, Hq, D], k/v [S, Hkv, D] on one GPU, D in {64, 128, 256}.
 
-    Q == S is a whole prefill (fa_prefill); Q < S is a chunk of Q new tokens
-    at positions S - Q .. S - 1 over a KV cache of S tokens (fa_prefill_chunk).
-    Allocates ``out`` (f32 [Q, Hq, 128]) unless given, enqueues the kernel on
-    ``stream`` (default: torch's current stream) and returns ``out``.
+    q, k, v are float16 or bfloat16 (all the same).  Q == S is a whole
+    prefill; Q < S is a chunk of Q new tokens at positions S - Q .. S - 1
+    over a KV cache of S tokens.  The output is float32 by default, or
+    ``out_dtype`` = q's dtype.  Allocates ``out`` ([Q, Hq, D]) unless given,
+    enqueues the kernel on ``stream`` (default: torch's current stream) and
+    returns ``out``.  f16 in / f32 out goes through fa_prefill or
+    fa_prefill_chunk, every other combination through fa_prefill_ex.
     """
     import torch
 
+    codes = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16, torch.float32: FA_DTYPE_F32}
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be [seq_len, heads, head_dim]")
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"q must be float16 or bfloat16, got {q.dtype}")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.float16:
-            raise TypeError(f"{name} must be float16, got {t.dtype}")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must be {q.dtype}, got {t.dtype}")
         if not t.is_cuda:
             raise ValueError(f"{name} must be on the GPU")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out_dtype not in (torch.float32, q.dtype):
+        raise TypeError(f"out_dtype must be float32 or {q.dtype}, got {out_dtype}")
     Q, n_q, hd = q.shape
     S = k.shape[0]
     if k.shape != v.shape or S < Q or k.shape[2] != hd:
@@ -201,20 +230,25 @@ def attention(q, k, v, scale: float, causal: bool = True, out=None, stream=None)
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k, v must be on the same device")
     if out is None:
-        out = torch.empty((Q, n_q, hd), dtype=torch.float32, device=q.device)
-    elif out.dtype != torch.float32 or out.shape != (Q, n_q, hd) or not out.is_contiguous() \
+        out = torch.empty((Q, n_q, hd), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or out.shape != (Q, n_q, hd) or not out.is_contiguous() \
             or out.device != q.device:
-        raise ValueError("out must be contiguous float32 [q_len, n_q_heads, head_dim] on q's device")
+        raise ValueError(f"out must be contiguous {out_dtype} [q_len, n_q_heads, head_dim] on q's device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    c = 1 if causal else 0
     with torch.cuda.device(q.device):
-        if Q == S:
-            status = fa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), n_q,
-                                k.shape[1], S, hd, scale, 1 if causal else 0, handle)
+        if q.dtype == torch.float16 and out_dtype == torch.float32:
+            if Q == S:
+                status = fa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), n_q,
+                                    k.shape[1], S, hd, scale, c, handle)
+            else:
+                status = fa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), n_q,
+                                          k.shape[1], Q, S, hd, scale, c, handle)
         else:
-            status = fa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), n_q,
-                                      k.shape[1], Q, S, hd, scale, 1 if causal else 0, handle)
+            status = fa_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), n_q,
+                                   k.shape[1], Q, S, hd, scale, c, codes[q.dtype], codes[out_dtype], handle)
     _check(status)
     return out
 

@@ -2,8 +2,9 @@
 
     python -m prefill_attention_amd.build        # or __graft_entry__.build()
 
-The HIP translation units (attention, K/V producer) are compiled for
-gfx950 only; the planner is plain C++.  Packed-FP32 VALU forms are disabled for the device code.
+The HIP translation units (the attention's host launcher, one kernel unit per
+head dimension, the K/V producer) are compiled for gfx950 only, in parallel;
+the planner is plain C++.  Packed-FP32 VALU forms are disabled for the device code.
 """
 
 from __future__ import annotations
@@ -35,17 +36,21 @@ def _run(cmd):
     subprocess.run(cmd, check=True)
 
 
+HIP_SOURCES = ("fa_prefill.hip", "fa_prefill_hd64.hip", "fa_prefill_hd128.hip", "fa_prefill_hd256.hip",
+               "fa_kv_store.hip")
+
+
 def build(verbose_resources: bool = False) -> str:
     """Compile the library; return its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     common = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
     plan_o = os.path.join(BUILD_DIR, "fa_plan.o")
-    kern_o = os.path.join(BUILD_DIR, "fa_prefill.o")
     cxx = shutil.which("g++") or shutil.which("c++")
     if cxx is None:
         raise RuntimeError("a host C++ compiler (g++) is required")
-    _run([cxx, *common, "-c", os.path.join(CSRC, "fa_plan.cpp"), "-o", plan_o])
     dev_flags = [
         f"--offload-arch={ARCH}",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -53,11 +58,18 @@ def build(verbose_resources: bool = False) -> str:
     ]
     if verbose_resources:
         dev_flags += ["-Rpass-analysis=kernel-resource-usage"]
-    _run([hipcc, *common, *dev_flags, "-c", os.path.join(CSRC, "fa_prefill.hip"), "-o", kern_o])
-    store_o = os.path.join(BUILD_DIR, "fa_kv_store.o")
-    _run([hipcc, *common, *dev_flags, "-c", os.path.join(CSRC, "fa_kv_store.hip"), "-o", store_o])
+    jobs = [[cxx, *common, "-c", os.path.join(CSRC, "fa_plan.cpp"), "-o", plan_o]]
+    objs = [plan_o]
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        jobs.append([hipcc, *common, *dev_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for f in [ex.submit(_run, cmd) for cmd in jobs]:
+            f.result()
     tmp = LIB_PATH + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", plan_o, kern_o, store_o, "-o", tmp])
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -167,7 +167,7 @@ bool overlap(const void* a, unsigned long long a_bytes, const void* b, unsigned 
 int current_device() {
     int dev = 0, n_cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(FA_ERR_DEVICE, "hipGetDevice failed");
-    return check_device(dev, &n_cus);
+    return check_device(dev, &n_cus, nullptr);
 }
 
 int launch_status(const char* what) {

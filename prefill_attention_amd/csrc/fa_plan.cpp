@@ -43,9 +43,17 @@ long long workspace_lw_offset(long long cap_items) { return ((cap_items * 4 + 25
 long long workspace_o_offset(long long cap_items, long long cap_parts) {
     return workspace_lw_offset(cap_items) + cap_parts * (long long)kQTile * 4;
 }
-long long workspace_bytes(long long cap_items, long long cap_parts) {
-    return cap_parts == 0 ? 0
-                          : workspace_o_offset(cap_items, cap_parts) + cap_parts * (long long)kQTile * kHeadDim * 4;
+long long workspace_bytes(long long cap_items, long long cap_parts, long long cap_o) {
+    return cap_parts == 0 ? 0 : workspace_o_offset(cap_items, cap_parts) + cap_o * 4;
+}
+
+int check_dtypes(int in_dtype, int out_dtype) {
+    if (in_dtype != FA_DTYPE_F16 && in_dtype != FA_DTYPE_BF16)
+        return fail(FA_ERR_DTYPE, "input dtype %d unsupported (f16 or bf16)", in_dtype);
+    if (out_dtype != FA_DTYPE_F32 && out_dtype != in_dtype)
+        return fail(FA_ERR_DTYPE, "output dtype %d unsupported (f32 or the input dtype %d)", out_dtype,
+                    in_dtype);
+    return FA_OK;
 }
 
 // Split-KV count for a launch of `items` query tiles.  Splitting pays only
@@ -59,8 +67,8 @@ long long workspace_bytes(long long cap_items, long long cap_parts) {
 // tile must run on one XCD (they meet through its L2), which the XCD-wise
 // head assignment guarantees when the head count is a multiple of 8.
 static int choose_splits(long long items, long long q_off, long long kv_len, bool causal, int n_q_heads,
-                         int n_cus) {
-    const long long slots = (long long)kGroupsPerCu * n_cus;
+                         int n_cus, int head_dim) {
+    const long long slots = (long long)groups_per_cu(head_dim) * n_cus;
     if (items <= 0 || items * 2 > slots || n_q_heads % kXcds != 0) return 1;
     // tiles shared out, for the tile with the fewest (the first query tile)
     const long long shared = causal ? q_off / kKvTile + 1 : (kv_len + kKvTile - 1) / kKvTile;
@@ -82,25 +90,26 @@ int make_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim
     if (n_q_heads % n_kv_heads != 0)
         return fail(FA_ERR_SHAPE, "n_q_heads %d is not a multiple of n_kv_heads %d", n_q_heads,
                     n_kv_heads);
+    if (!head_dim_supported(head_dim))
+        return fail(FA_ERR_HEAD_DIM, "head_dim %d unsupported (64, 128 or 256)", head_dim);
     // a 64-row K/V tile of one head must be addressable with 31-bit buffer offsets
-    if ((long long)n_kv_heads * kRowBytes * kKvTile > INT_MAX)
+    if ((long long)n_kv_heads * row_bytes(head_dim) * kKvTile > INT_MAX)
         return fail(FA_ERR_SHAPE, "n_kv_heads %d too large (row stride overflows buffer offsets)",
                     n_kv_heads);
-    if (head_dim != kHeadDim)
-        return fail(FA_ERR_HEAD_DIM, "head_dim %d unsupported (only %d)", head_dim, kHeadDim);
     long long n_q_tiles = ((long long)q_len + kQTile - 1) / kQTile;
     long long n_groups = n_q_tiles * (long long)n_q_heads;
     if (n_groups > INT_MAX)
         return fail(FA_ERR_SHAPE, "grid of %lld work-groups exceeds the launch limit", n_groups);
     // element offsets of the largest tensor must fit a signed 64-bit range
-    if ((long long)kv_len * n_q_heads > (LLONG_MAX / 4) / kHeadDim)
+    if ((long long)kv_len * n_q_heads > (LLONG_MAX / 4) / head_dim)
         return fail(FA_ERR_SHAPE, "tensor too large");
-    if (max_lds_bytes > 0 && kLdsBytes > max_lds_bytes)
+    if (max_lds_bytes > 0 && lds_bytes(head_dim) > max_lds_bytes)
         return fail(FA_ERR_RESOURCE, "kernel needs %d B of LDS per work-group, device allows %d",
-                    kLdsBytes, max_lds_bytes);
+                    lds_bytes(head_dim), max_lds_bytes);
     if (n_cus <= 0) n_cus = 256;
     const long long items = n_q_tiles * (long long)n_q_heads;
-    const int splits = choose_splits(items, (long long)kv_len - q_len, kv_len, causal != 0, n_q_heads, n_cus);
+    const int splits = choose_splits(items, (long long)kv_len - q_len, kv_len, causal != 0, n_q_heads, n_cus,
+                                     head_dim);
     if (items * splits > INT_MAX)
         return fail(FA_ERR_SHAPE, "grid of %lld work-groups exceeds the launch limit", items * splits);
     if (plan) {
@@ -111,11 +120,13 @@ int make_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim
         plan->kv_splits = splits;
         plan->n_q_tiles = (int)n_q_tiles;
         plan->n_groups = items * splits;
-        plan->workspace_bytes = splits > 1 ? workspace_bytes(items, items * splits) : 0;
+        plan->workspace_bytes =
+            splits > 1 ? workspace_bytes(items, items * splits, items * splits * (long long)kQTile * head_dim) : 0;
         plan->stages = kStages;
-        plan->lds_bytes = kLdsBytes;
-        plan->lds_k_bytes = kLdsKBytes;
-        plan->lds_v_bytes = kLdsVBytes;
+        plan->lds_bytes = lds_bytes(head_dim);
+        plan->lds_k_bytes = lds_k_bytes(head_dim);
+        plan->lds_v_bytes = lds_v_bytes(head_dim);
+        plan->groups_per_cu = groups_per_cu(head_dim);
         long long tiles = 0;
         for (long long t = 0; t < n_q_tiles; ++t)
             tiles += tiles_for_group(t * kQTile, (long long)kv_len - q_len, kv_len, causal != 0);
@@ -124,8 +135,8 @@ int make_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim
     return FA_OK;
 }
 
-int validate_call(const void* q, const void* k, const void* v, const float* out, int n_q_heads,
-                  int n_kv_heads, int q_len, int kv_len, int head_dim, float scale) {
+int validate_call(const void* q, const void* k, const void* v, const void* out, int n_q_heads,
+                  int n_kv_heads, int q_len, int kv_len, int head_dim, float scale, int out_bytes) {
     if (q_len > 0 && (!q || !k || !v || !out))
         return fail(FA_ERR_NULL, "a tensor pointer is NULL");
     if (!std::isfinite(scale)) return fail(FA_ERR_SCALE, "scale is not finite");
@@ -136,7 +147,7 @@ int validate_call(const void* q, const void* k, const void* v, const float* out,
     // overlap of out with an input
     const unsigned long long Q = (unsigned long long)q_len, S = (unsigned long long)kv_len;
     const unsigned long long ob = reinterpret_cast<unsigned long long>(out);
-    const unsigned long long oe = ob + Q * n_q_heads * head_dim * 4ull;
+    const unsigned long long oe = ob + Q * n_q_heads * head_dim * (unsigned long long)out_bytes;
     struct Span { const void* p; unsigned long long bytes; } in[3] = {
         {q, Q * n_q_heads * head_dim * 2ull},
         {k, S * n_kv_heads * head_dim * 2ull},
@@ -170,7 +181,7 @@ const char* fa_prefill_strerror(int status) {
         case FA_OK: return "success";
         case FA_ERR_NULL: return "a tensor pointer is NULL";
         case FA_ERR_SHAPE: return "invalid shape (lengths, head counts or grid size)";
-        case FA_ERR_HEAD_DIM: return "unsupported head_dim (only 128)";
+        case FA_ERR_HEAD_DIM: return "unsupported head_dim (64, 128 or 256)";
         case FA_ERR_SCALE: return "scale is not finite";
         case FA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
         case FA_ERR_RESOURCE: return "launch plan exceeds a device resource limit";
@@ -178,6 +189,7 @@ const char* fa_prefill_strerror(int status) {
         case FA_ERR_ALIAS: return "output overlaps an input";
         case FA_ERR_DEVICE: return "no usable gfx950 device";
         case FA_ERR_WORKSPACE: return "workspace allocation or release failed";
+        case FA_ERR_DTYPE: return "unsupported input or output element type";
         default: return "unknown fa_prefill status";
     }
 }

@@ -1,65 +1,7 @@
-// Causal prefill flash-attention for MI355X (gfx950 / CDNA4), and the C-ABI
-// entry point that launches it.
-//
-// What it computes: out = softmax(scale * Q K^T + causal mask) V per head,
-// f16 Q/K/V, f32 accumulation, f32 output, with a tiled online softmax (the
-// pages' fa_prefill_f16kv: "49 · r46 (FAP1) — FA audit", §2.1; its per-tile
-// lifecycle in "53 · r50 — FA_TKV 32→16 occupancy experiment", §2).
-//
-// How it maps onto CDNA4 (the pages' wmma / cp.async design was for another
-// GPU; only its ideas carry over):
-//
-//  * A work-group of 4 wavefronts owns 128 query rows of one head; each
-//    wavefront owns 32 of them.  It walks the key/value sequence in tiles of
-//    64 rows and stops at the causal bound, so tiles above the diagonal are
-//    never visited (the pages' KV loop bound, "53 · r50", §3.2).
-//
-//  * K and V tiles go from HBM/L2 straight into LDS with buffer loads that
-//    write LDS directly (no register staging).  The buffer descriptor's
-//    record count ends at the last stored key, so rows past kv_len read as
-//    zeros in hardware (the pages zero-fill them explicitly, "53 · r50", §2).
-//    Two LDS stages: tile j+1 streams in while tile j is computed, with one
-//    work-group barrier per tile.
-//
-//  * LDS rows are the unpadded 256-byte K/V rows; the 16-byte chunk c of key
-//    row r is stored at chunk c ^ swz(r).  This replaces the pages' +8-half
-//    row padding ("11 · P5 — prefill gap session", §2.2) because the
-//    direct-to-LDS loads write 1 KiB contiguously per instruction, and it
-//    keeps both read patterns below free of bank conflicts.
-//
-//  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_f16:
-//    K (from LDS) is the A operand, Q^T (registers, loaded once) is B.  In the
-//    32x32 accumulator a lane holds one column — one query — and 16 of the
-//    32 keys.  So the softmax state of a query lives in one lane pair
-//    (lane, lane^32): row max and row sum are in-lane reductions plus one
-//    v_permlane32_swap, and the probabilities of a lane are already laid out
-//    as the B operand (k = key, n = query) of O^T = V^T P^T.  P never leaves
-//    the registers (the register-resident softmax idea of the pages' FAP2,
-//    "49 · r46", §5, and "11 · P5", §3.2, re-derived for the CDNA layout).
-//
-//  * The A operand of O^T = V^T P^T (head-dim x keys) is read from the
-//    key-major V tile with ds_read_b64_tr_b16, whose 16-lane transpose turns
-//    four 8-byte row pieces into four keys of one head-dim column per lane.
-//
-//  * Softmax in base 2: p = 2^(s*scale*log2(e) - m).  The running reference
-//    m is only raised when a tile's maximum exceeds it by more than 8 (log2
-//    units), so p <= 256 stays far inside f16 range; otherwise O and l are
-//    not rescaled at all.  O/l is unchanged in exact arithmetic by the choice
-//    of reference, so the result is the same softmax.
-//
-//  * The validity predicate is "key <= the query's position (causal) and
-//    key < kv_len", both bounds always applied (the pages' tail-tile
-//    lane-mask bug, "28 · r23", §2.3), but only on tiles that touch the
-//    diagonal or the end of the keys; every other tile runs unmasked.  Query
-//    row r is at position kv_len - q_len + r: the whole sequence for a
-//    prefill, the last q_len positions for a chunk appended to a KV cache
-//    (the pages compare keys with a query position against a stored-KV end,
-//    "28 · r23", §3.2, and write each token's K/V at its position, "11 · P5",
-//    §3.2).
-//
-//  * Work-group order: the heaviest query tiles first; when the head count is
-//    a multiple of 8, the 8 XCDs (which receive work-groups round-robin) each
-//    own a contiguous range of heads, so one kv head's K/V stays in one L2.
+// Host side of the prefill attention: device checks, the split-KV
+// workspace, and the launch of the kernel variant a call needs.  The kernel
+// itself is the template in fa_prefill_kernel.h, instantiated per head
+// dimension in fa_prefill_hd64/128/256.hip.
 
 #include <hip/hip_runtime.h>
 
@@ -74,544 +16,23 @@
 #include "fa_internal.h"
 
 namespace fa {
-namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef float floatx2 __attribute__((ext_vector_type(2)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) short4v lds_short4;
-
-// Lazy-rescale threshold in log2 units: probabilities stay <= 2^8.
-constexpr float kTau = 8.0f;
-// Buffer descriptor word 3 for raw (untyped) dword access on CDNA.
-constexpr int kBufferFlags = 0x00020000;
-
-__device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-// Chunk permutation of key row r: ((r & 3) << 2) | ((r >> 2) & 3).  Sixteen
-// consecutive rows map one logical chunk to 16 distinct chunks (the K
-// operand reads: 16 lanes x 16 B); four consecutive rows map four
-// neighbouring chunks to 16 distinct chunks (the transposed V reads: 32
-// lanes x 8 B cover 4 rows x 64 B), so neither read pattern has a bank
-// conflict on 64 banks of 4 bytes.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-// max / sum of x over the lane pair (lane, lane ^ 32).  v_permlane32_swap
-// exchanges the upper half of its first operand with the lower half of its
-// second; with both operands = x the two results hold x and the partner
-// lane's x, in some order, in every lane.
-__device__ __forceinline__ float pair_max(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Key (within the tile) held by accumulator register i of 32-key block kb in
-// lane group g: the 32x32 MFMA result row index.
-__device__ __forceinline__ int acc_key(int kb, int i, int g) {
-    return 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-}
-
-// Copy key/value rows [kt, kt + 64) of head hk from src (f16
-// [kv_len][n_kv][128]) into an LDS tile; this wavefront copies rows 16*wave .. 16*wave + 15, four
-// rows (1 KiB) per instruction.  Lane i of an instruction fills physical
-// chunk i % 16 of its row, so it loads logical chunk (i % 16) ^ swz(row).
-__device__ __forceinline__ void stage_tile(const _Float16* __restrict__ src, int n_kv, int hk,
-                                           int kv_len, int kt, char* tile, int wave, int lane) {
-    const uint32_t row_bytes = (uint32_t)n_kv * kRowBytes;
-    const char* base = reinterpret_cast<const char*>(src) + (size_t)kt * row_bytes +
-                       (size_t)hk * kRowBytes;
-    // Bytes addressable from base: up to the end of the last valid row of
-    // this head, so rows >= kv_len fall outside the record and read as 0.
-    const long long valid = (long long)(kv_len - kt) * row_bytes - (long long)hk * kRowBytes;
-    const long long cap = (long long)kKvTile * row_bytes;
-    const uint32_t n_records = (uint32_t)(valid < cap ? valid : cap);
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)n_records, kBufferFlags);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row0 = 16 * wave + 4 * j;
-        const int row = row0 + (lane >> 4);
-        const int chunk = (lane & 15) ^ swz(row);
-        const uint32_t voff = (uint32_t)row * row_bytes + (uint32_t)chunk * 16u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + row0 * kRowBytes), 16, voff,
-                                                 0, 0, 0);
-    }
-}
-
-// A operand of O^T += V^T P^T for head-dim block db and key step ks: the
-// 32 x 16 slice V^T[32db .. 32db+31][16ks .. 16ks+15] in the slot order of
-// the probability registers (slot (g, e) <-> key 16ks + 8(e/4) + 4g + e%4).
-// Two transposed reads (h = 0, 1): within each 16-lane group, lane i = 4r +
-// qd addresses key 16ks + 8h + 4g + r, head-dim columns 4(i%4) .. +3 of the
-// group's 16 columns, and receives column i of the four keys.
-//
-// The key's swizzle, 4r + 2h + g, does not depend on ks, so the byte offset
-// splits into a per-lane part for each (db, h) -- vt_lane_offset, computed
-// once -- and 4096 ks, which the LDS instruction takes as an immediate.
-__device__ __forceinline__ int vt_lane_offset(int db, int h, int l32, int g) {
-    const int i = l32 & 15;
-    const int r = i >> 2, qd = i & 3;
-    const int chunk = 4 * db + 2 * (l32 >> 4) + (qd >> 1);
-    const int key = 8 * h + 4 * g + r;
-    return key * kRowBytes + ((chunk ^ swz(key)) << 4) + ((qd & 1) << 3);
-}
-
-__device__ __forceinline__ half8 load_vt(const char* vtile, const int (&vt_off)[8], int db, int ks) {
-    half8 a;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const char* p = vtile + 16 * ks * kRowBytes + vt_off[2 * db + h];
-        const short4v t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
-        const half4 hv = __builtin_bit_cast(half4, t);
-        a[4 * h + 0] = hv[0];
-        a[4 * h + 1] = hv[1];
-        a[4 * h + 2] = hv[2];
-        a[4 * h + 3] = hv[3];
-    }
-    return a;
-}
-
-// Scores of one 64-key tile for this wavefront's 32 queries: S^T blocks for
-// keys [0, 32) and [32, 64) of the tile.
-struct TileScores {
-    floatx16 b[2];
-};
-
-// Mask the scores of tile t: -inf where the key is past the stored keys or
-// (causal) after the query's position.  Only tiles on the diagonal or at the
-// end of the keys need it.
-template <bool CAUSAL>
-__device__ __forceinline__ void mask_scores(TileScores& s, int t, int q_pos, int kv_len, int g) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = t * kKvTile + acc_key(kb, i, g);
-            const bool ok = key < kv_len && (!CAUSAL || key <= q_pos);
-            s.b[kb][i] = ok ? s.b[kb][i] : -INFINITY;
-        }
-}
-
-// Whether tile t needs the mask for a wavefront whose first query is at
-// position pos_w.
-template <bool CAUSAL>
-__device__ __forceinline__ bool tile_needs_mask(int t, int pos_w, int kv_len) {
-    return (t * kKvTile + kKvTile > kv_len) ||
-           (CAUSAL && t * kKvTile + kKvTile - 1 > pos_w);
-}
-
-// Phase A of the tile pipeline, as 16 explicit issue slots.  Slot i
-// (kb = i / 8, t = i % 8):
-//   MFMA (when HAS_NEXT): S^T block kb of the next tile += K fragment t x Q^T
-//     fragment t; the K fragment was read from LDS four slots earlier into
-//     one of four rotating registers, and the read for slot i + 4 is issued
-//     right after;
-//   VALU (when HAS_CUR): two probabilities of the current tile, p = 2^(s*c2
-//     - m) rounded to f16 into the B operands of O^T += V^T P^T, and their
-//     contribution to the row sum.
-// With PREFETCH_V the last four slots also read phase B's first four V^T
-// fragments.  Hard scheduling barriers between slots keep every K read four
-// MFMAs ahead of its use and the exponentials spread under the MFMAs.
-template <bool HAS_CUR, bool HAS_NEXT, bool PREFETCH_V>
-__device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next, const half8 (&qb)[8],
-                                        const TileScores& sc, TileScores& sn, half8 (&pb)[4],
-                                        float& l_part, float m_ref, float c2, int l32, int g,
-                                        const char* __restrict__ vtile, const int (&vt_off)[8],
-                                        half8 (&vf)[4]) {
-    float lsum = 0.0f;
-    const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
-    // K fragment (kb, t): key row 32kb + l32, head-dim 16t + 8g.
-    const int z = swz(l32);  // swz(32kb + l32) == swz(l32)
-    const char* rp = ktile_next + l32 * kRowBytes;
-    auto kread = [&](int i) {
-        const int kb = i >> 3, t = i & 7;
-        return *reinterpret_cast<const half8*>(rp + kb * 32 * kRowBytes + (((2 * t + g) ^ z) << 4));
-    };
-    // VALU chunk c: probabilities 2c and 2c + 1 of the current tile.
-    auto valu_chunk = [&](int c) {
-        const int kb = c >> 3, e = 2 * (c & 7);
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc.b[kb][e], c2, -m_ref));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc.b[kb][e + 1], c2, -m_ref));
-        const floatx2 pf = {p0, p1};
-        const half2v ph = __builtin_convertvector(pf, half2v);
-        pb[2 * kb + (e >> 3)][e & 7] = ph[0];
-        pb[2 * kb + (e >> 3)][(e & 7) + 1] = ph[1];
-        lsum = __builtin_amdgcn_fdot2(ph, ones, lsum, false);
-    };
-    half8 kf[4];
-    floatx16 acc[2] = {};
-    if (HAS_NEXT) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kf[i] = kread(i);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (HAS_NEXT) {
-            acc[i >> 3] = mfma32(kf[i & 3], qb[i & 7], acc[i >> 3]);
-            if (i + 4 < 16) kf[i & 3] = kread(i + 4);
-        }
-        // The first four V^T fragments of phase B, read while the K reads wind down.
-        if (PREFETCH_V && i >= 12) vf[i - 12] = load_vt(vtile, vt_off, i - 12, 0);
-        if (HAS_CUR) valu_chunk(i);
-    }
-    if (HAS_CUR && HAS_NEXT) {
-        // Register fences: keep the probabilities in this phase (code
-        // motion before scheduling would otherwise sink them into phase B).
-#pragma unroll
-        for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[i]));
-        asm volatile("" : "+v"(lsum));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (HAS_NEXT) {
-        sn.b[0] = acc[0];
-        sn.b[1] = acc[1];
-    }
-    l_part += lsum;
-}
-
-// Phase B, as 16 explicit issue slots.  Slot f (ks = f / 4, db = f % 4):
-// MFMA O^T block db += V^T fragment (db, ks) x P^T fragment ks, the V^T
-// fragment (two transposed LDS reads) having been read four slots earlier
-// (the first four in phase A), then the read for slot f + 4.  VALU (when
-// HAS_NEXT): the next tile's row maximum, returned in log2 units (-inf if the
-// tile has no visible key for the query), spread over the slots.
-template <bool HAS_NEXT>
-__device__ __forceinline__ float phase_b(const char* __restrict__ vtile, const half8 (&pb)[4],
-                                         floatx16 (&oacc)[4], const TileScores& sn, float c2,
-                                         int l32, int g, const int (&vt_off)[8], half8 (&vf)[4]) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int f = 0; f < 16; ++f) {
-        __builtin_amdgcn_sched_barrier(0);
-        oacc[f & 3] = mfma32(vf[f & 3], pb[f >> 2], oacc[f & 3]);
-        if (f + 4 < 16) vf[f & 3] = load_vt(vtile, vt_off, (f + 4) & 3, (f + 4) >> 2);
-        if (HAS_NEXT) {
-            const int kb = f >> 3, i = 2 * (f & 7);
-            mx = fmaxf(fmaxf(mx, sn.b[kb][i]), sn.b[kb][i + 1]);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    float mt = -INFINITY;
-    if (HAS_NEXT) {
-        mx = pair_max(mx);
-        mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
-    }
-    return mt;
-}
-
-// Raise the softmax reference when some query's tile maximum outgrew it by
-// more than tau; O and l are rescaled by 2^(m_old - m_new) in that case only.
-__device__ __forceinline__ void maybe_rescale(float mt, float& m_ref, float& l_part,
-                                              floatx16 (&oacc)[4]) {
-    if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau)) {
-        const float m_new = fmaxf(m_ref, mt);
-        // A side effect keeps this rarely taken block from being speculated
-        // (the compiler would otherwise multiply by alpha = 1 on every tile).
-        // The multiplies themselves stay ordinary code: they read MFMA
-        // results, and only visible code gets the MFMA-to-VALU wait states.
-        asm volatile("" ::: "memory");
-        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-        m_ref = m_new;
-    }
-}
-
-template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
-    const _Float16* __restrict__ q, const _Float16* __restrict__ k, const _Float16* __restrict__ v,
-    float* __restrict__ out, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int n_q_tiles,
-    float c2, int q_mode, int n_splits, int* __restrict__ ws_ctr, float* __restrict__ ws_lw,
-    float* __restrict__ ws_o) {
-    __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
-    // K tile i lives in kbuf(i), V tile i in vbuf(i): two buffers each (i counts
-    // the tiles of this work-group's key range).
-    char* const kstage = lds;
-    char* const vstage = lds + kLdsKBytes;
-    int* const merge_flag = reinterpret_cast<int*>(lds + kLdsKBytes + kLdsVBytes);
-    auto kbuf = [&](int t) { return kstage + (t & 1) * kTileBytes; };
-    auto vbuf = [&](int t) { return vstage + (t & 1) * kTileBytes; };
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWaveSize - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWaveSize);
-    const int l32 = lane & 31;
-    const int g = lane >> 5;
-
-    // Work-group -> (head, query tile, key-range part): heaviest query tiles
-    // first; with a head count divisible by the XCD count, XCD x (= blockIdx
-    // % 8) owns heads [x*H/8, (x+1)*H/8), so one kv head's K/V stays in one
-    // L2 and all parts of a split query tile meet in that L2.  (Other head
-    // counts are never split.)
-    const int b = blockIdx.x;
-    int h, rank, split = 0;
-    if ((n_q_heads % kXcds) == 0) {
-        const int per_xcd = n_q_heads / kXcds;
-        const int local = b / kXcds;
-        rank = local / (per_xcd * n_splits);
-        const int rem = local % (per_xcd * n_splits);
-        split = rem / per_xcd;
-        h = (b % kXcds) * per_xcd + rem % per_xcd;
-    } else {
-        h = b % n_q_heads;
-        rank = b / n_q_heads;
-    }
-    const int qt = CAUSAL ? n_q_tiles - 1 - rank : rank;
-    const int hk = h / (n_q_heads / n_kv_heads);
-    const int q0 = qt * kQTile;
-    const int qw = q0 + wave * kQRowsPerWave;
-    const int my_q = qw + l32;  // query row (index into q and out)
-    // Query row r sits at sequence position q_off + r: a chunk of q_len new
-    // tokens follows kv_len - q_len tokens already in the KV cache (q_off = 0
-    // for a whole prefill).
-    const int q_off = kv_len - q_len;
-    const int pos_w = q_off + qw;
-    const int q_pos = q_off + my_q;
-
-    const int kv_end = CAUSAL ? min(kv_len, q_off + q0 + kQTile) : kv_len;
-    const int n_all = (kv_end + kKvTile - 1) / kKvTile;
-    // Key tiles [t_lo, t_lo + n_tiles) of this work-group.  A split tile's
-    // parts share out the tiles that start at or before the tile's first
-    // query position (so every query row sees a key in every part); the last
-    // part also takes the diagonal and tail tiles.
-    int t_lo = 0, n_tiles = n_all;
-    if (n_splits > 1) {
-        const int shared = CAUSAL ? (q_off + q0) / kKvTile + 1 : n_all;
-        t_lo = split * shared / n_splits;
-        n_tiles = (split == n_splits - 1 ? n_all : (split + 1) * shared / n_splits) - t_lo;
-    }
-    auto kv_row = [&](int i) { return (t_lo + i) * kKvTile; };
-
-    // Staging schedule: K tile t is copied two tiles ahead of its use in
-    // phase A, V tile t one tile ahead of its use in phase B.
-    stage_tile(k, n_kv_heads, hk, kv_len, kv_row(0), kbuf(0), wave, lane);
-    stage_tile(v, n_kv_heads, hk, kv_len, kv_row(0), vbuf(0), wave, lane);
-    if (n_tiles > 1) stage_tile(k, n_kv_heads, hk, kv_len, kv_row(1), kbuf(1), wave, lane);
-
-    // Q^T as the B operand: lane (l32, g) holds q[my_q][h][16t + 8g .. +8).
-    // q_mode 1 negates Q (negative scale), 2 zeroes it (scale 0).
-    half8 qb[8];
-    {
-        const bool in = my_q < q_len && q_mode != 2;
-        const _Float16* qrow = q + ((size_t)my_q * n_q_heads + h) * kHeadDim + 8 * g;
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            qb[t] = in ? *reinterpret_cast<const half8*>(qrow + 16 * t) : half8{};
-        if (q_mode == 1) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) qb[t] = -qb[t];
-        }
-    }
-
-    int vt_off[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) vt_off[i] = vt_lane_offset(i >> 1, i & 1, l32, g);
-
-    floatx16 oacc[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[db] = floatx16{};
-    float m_ref = -INFINITY, l_part = 0.0f;
-    half8 pb[4];
-    TileScores sa, sb;
-
-    // Prologue: scores and reference maximum of tile 0.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    {
-        half8 vf_unused[4];
-        phase_a<false, true, false>(kbuf(0), qb, sa, sa, pb, l_part, m_ref, c2, l32, g, nullptr, vt_off, vf_unused);
-        if (tile_needs_mask<CAUSAL>(t_lo, pos_w, kv_len)) mask_scores<CAUSAL>(sa, t_lo, q_pos, kv_len, g);
-        float mx = fmaxf(sa.b[0][0], sa.b[1][0]);
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sa.b[0][i], sa.b[1][i]));
-        mx = pair_max(mx);
-        maybe_rescale((mx == -INFINITY) ? -INFINITY : mx * c2, m_ref, l_part, oacc);
-    }
-
-    // Pipeline step for tile j (its scores in sc), producing the scores of
-    // tile j + 1 in sn.  On entry K(j+1) and V(j) have been issued; the
-    // barrier also frees kbuf(j) and vbuf(j - 1) for K(j+2) and V(j+1).
-    auto step = [&](int j, TileScores& sc, TileScores& sn) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (j + 2 < n_tiles) stage_tile(k, n_kv_heads, hk, kv_len, kv_row(j + 2), kbuf(j + 2), wave, lane);
-        stage_tile(v, n_kv_heads, hk, kv_len, kv_row(j + 1), vbuf(j + 1), wave, lane);
-        half8 vf[4];
-        phase_a<true, true, true>(kbuf(j + 1), qb, sc, sn, pb, l_part, m_ref, c2, l32, g, vbuf(j), vt_off, vf);
-        if (tile_needs_mask<CAUSAL>(t_lo + j + 1, pos_w, kv_len))
-            mask_scores<CAUSAL>(sn, t_lo + j + 1, q_pos, kv_len, g);
-        const float mt = phase_b<true>(vbuf(j), pb, oacc, sn, c2, l32, g, vt_off, vf);
-        maybe_rescale(mt, m_ref, l_part, oacc);
-    };
-    // Last tile: probabilities and P.V only.
-    auto last = [&](int j, TileScores& sc) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        half8 vf[4];
-        phase_a<true, false, true>(nullptr, qb, sc, sc, pb, l_part, m_ref, c2, l32, g, vbuf(j), vt_off, vf);
-        phase_b<false>(vbuf(j), pb, oacc, sc, c2, l32, g, vt_off, vf);
-    };
-
-    int j = 0;
-    for (; j + 2 < n_tiles; j += 2) {
-        step(j, sa, sb);
-        step(j + 1, sb, sa);
-    }
-    if (j + 1 < n_tiles) {
-        step(j, sa, sb);
-        last(j + 1, sb);
-    } else {
-        last(j, sa);
-    }
-
-    // Epilogue, rows < q_len only.  Lane (l32, g), register i of block db
-    // holds head-dim 32*db + 8*(i/4) + 4*g + i%4.
-    const float l_tot = pair_sum(l_part);
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    float* const orow = out + ((size_t)my_q * n_q_heads + h) * kHeadDim + 4 * g;
-    if (n_splits == 1) {
-        if (my_q < q_len) {
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const floatx4 o = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv,
-                                       oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv};
-                    *reinterpret_cast<floatx4*>(orow + 32 * db + 8 * jj) = o;
-                }
-        }
-        return;
-    }
-
-    // One part of a split query tile.  Publish its normalised output O / l
-    // and its log-weight lw = m + log2(l) (the softmax mass of its keys, in
-    // log2 units), then count arrivals; the last part to arrive combines all
-    // parts as out = sum_s w_s (O/l)_s / sum_s w_s with w_s = 2^(lw_s - max lw)
-    // -- the merge the online softmax applies between key tiles -- reading
-    // every part (its own included) from the workspace in part order, so the
-    // result does not depend on which part finished last.
-    const int item = h * n_q_tiles + qt;
-    const int row = wave * kQRowsPerWave + l32;
-    const size_t part0 = (size_t)item * n_splits;
-    if (my_q < q_len) {
-        float* const po = ws_o + ((part0 + split) * kQTile + row) * kHeadDim + 4 * g;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const floatx4 o = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv,
-                                   oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv};
-                *reinterpret_cast<floatx4*>(po + 32 * db + 8 * jj) = o;
-            }
-        if (g == 0)
-            ws_lw[(part0 + split) * kQTile + row] =
-                l_tot > 0.0f ? m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-    }
-    // All parts of this tile run on this XCD and meet in its L2: each wave
-    // waits until its stores have reached the L2 before the arrival is
-    // counted (an atomic performed in the L2), and the last part drops its
-    // CU's L1 lines before reading the others' results.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0)
-        *merge_flag = __hip_atomic_fetch_add(ws_ctr + item, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (*merge_flag != n_splits - 1) return;
-    asm volatile("buffer_inv sc0" ::: "memory");
-    if (tid == 0) __hip_atomic_store(ws_ctr + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (my_q < q_len) {
-        float wt[kMaxSplits];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int p = 0; p < kMaxSplits; ++p) {
-            wt[p] = p < n_splits ? ws_lw[(part0 + p) * kQTile + row] : -INFINITY;
-            mx = fmaxf(mx, wt[p]);
-        }
-        float wsum = 0.0f;
-#pragma unroll
-        for (int p = 0; p < kMaxSplits; ++p) {
-            wt[p] = p < n_splits ? __builtin_amdgcn_exp2f(wt[p] - mx) : 0.0f;
-            wsum += wt[p];
-        }
-        const float norm = 1.0f / wsum;
-        // Two halves of the head dimension; in each, the parts' values are
-        // loaded four parts at a time so their latencies overlap, and every
-        // sum runs in part order.
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            floatx4 acc[2][4];
-#pragma unroll
-            for (int d = 0; d < 2; ++d)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) acc[d][jj] = floatx4{};
-#pragma unroll
-            for (int p0 = 0; p0 < kMaxSplits; p0 += 4) {
-                if (p0 >= n_splits) break;
-                floatx4 x[4][2][4];
-#pragma unroll
-                for (int pp = 0; pp < 4; ++pp) {
-                    const int p = p0 + pp;
-                    if (p < n_splits) {
-                        const float* po = ws_o + ((part0 + p) * kQTile + row) * kHeadDim + 4 * g;
-#pragma unroll
-                        for (int d = 0; d < 2; ++d)
-#pragma unroll
-                            for (int jj = 0; jj < 4; ++jj)
-                                x[pp][d][jj] = *reinterpret_cast<const floatx4*>(po + 32 * (2 * hf + d) + 8 * jj);
-                    }
-                }
-#pragma unroll
-                for (int pp = 0; pp < 4; ++pp) {
-                    const int p = p0 + pp;
-                    if (p >= n_splits) break;
-#pragma unroll
-                    for (int d = 0; d < 2; ++d)
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) acc[d][jj][e] += wt[p] * x[pp][d][jj][e];
-                        }
-                }
-            }
-#pragma unroll
-            for (int d = 0; d < 2; ++d)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    *reinterpret_cast<floatx4*>(orow + 32 * (2 * hf + d) + 8 * jj) = acc[d][jj] * norm;
-        }
-    }
-}
-
-}  // namespace
-
-// Per-device check: gfx950 and the LDS limit, cached (0 unknown, 1 ok, else
-// the error), with the device's compute-unit count.
+// Per-device check: gfx950, cached (0 unknown, 1 ok, else the error), with
+// the device's compute-unit count and LDS limit per work-group.
 namespace {
 constexpr int kMaxDevices = 64;
 int g_device_state[kMaxDevices];
 int g_device_cus[kMaxDevices];
+long long g_device_lds[kMaxDevices];
 
 }  // namespace
 
-int check_device(int dev, int* n_cus) {
+int check_device(int dev, int* n_cus, long long* max_lds) {
     if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_DEVICE, "device index %d out of range", dev);
     int st = __atomic_load_n(&g_device_state[dev], __ATOMIC_ACQUIRE);
     if (st == 1) {
         *n_cus = __atomic_load_n(&g_device_cus[dev], __ATOMIC_RELAXED);
+        if (max_lds) *max_lds = __atomic_load_n(&g_device_lds[dev], __ATOMIC_RELAXED);
         return FA_OK;
     }
     if (st > 1) return fail(st, "device %d is not usable (see first error)", dev);
@@ -620,14 +41,13 @@ int check_device(int dev, int* n_cus) {
         return fail(FA_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
     int result = FA_OK;
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
-        result = fail(FA_ERR_DEVICE, "device %d is %s, the kernel is built for gfx950", dev,
+        result = fail(FA_ERR_DEVICE, "device %d is %s, the kernels are built for gfx950", dev,
                       prop.gcnArchName);
-    else if ((size_t)kLdsBytes > prop.sharedMemPerBlock)
-        result = fail(FA_ERR_RESOURCE, "kernel needs %d B of LDS, device allows %zu", kLdsBytes,
-                      prop.sharedMemPerBlock);
     __atomic_store_n(&g_device_cus[dev], prop.multiProcessorCount, __ATOMIC_RELAXED);
+    __atomic_store_n(&g_device_lds[dev], (long long)prop.sharedMemPerBlock, __ATOMIC_RELAXED);
     __atomic_store_n(&g_device_state[dev], result == FA_OK ? 1 : result, __ATOMIC_RELEASE);
     *n_cus = prop.multiProcessorCount;
+    if (max_lds) *max_lds = (long long)prop.sharedMemPerBlock;
     return result;
 }
 
@@ -640,7 +60,7 @@ struct WorkspaceBlock {
     int dev;
     void* stream;
     char* ptr;
-    long long cap_items, cap_parts;
+    long long cap_items, cap_parts, cap_o;
 };
 std::mutex g_ws_mu;
 std::vector<WorkspaceBlock> g_ws;
@@ -651,24 +71,26 @@ struct Workspace {
     float* o;
 };
 
-int acquire_workspace(int dev, void* stream, long long items, long long parts, Workspace* ws) {
+int acquire_workspace(int dev, void* stream, long long items, long long parts, long long o_floats,
+                      Workspace* ws) {
     std::lock_guard<std::mutex> lk(g_ws_mu);
     WorkspaceBlock* blk = nullptr;
     for (WorkspaceBlock& w : g_ws)
         if (w.dev == dev && w.stream == stream) blk = &w;
-    if (!blk || blk->cap_items < items || blk->cap_parts < parts) {
-        long long cap_items = items, cap_parts = parts;
+    if (!blk || blk->cap_items < items || blk->cap_parts < parts || blk->cap_o < o_floats) {
+        long long cap_items = items, cap_parts = parts, cap_o = o_floats;
         if (blk) {
             cap_items = std::max(cap_items, blk->cap_items);
             cap_parts = std::max(cap_parts, blk->cap_parts);
+            cap_o = std::max(cap_o, blk->cap_o);
             // Earlier kernels on this stream may still use the smaller block.
             if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess ||
                 hipFree(blk->ptr) != hipSuccess)
                 return fail(FA_ERR_WORKSPACE, "could not release the old workspace of device %d", dev);
             blk->ptr = nullptr;
-            blk->cap_items = blk->cap_parts = 0;
+            blk->cap_items = blk->cap_parts = blk->cap_o = 0;
         }
-        const size_t bytes = (size_t)workspace_bytes(cap_items, cap_parts);
+        const size_t bytes = (size_t)workspace_bytes(cap_items, cap_parts, cap_o);
         void* p = nullptr;
         if (hipMalloc(&p, bytes) != hipSuccess)
             return fail(FA_ERR_WORKSPACE, "hipMalloc of %zu B of workspace failed on device %d", bytes, dev);
@@ -677,12 +99,13 @@ int acquire_workspace(int dev, void* stream, long long items, long long parts, W
             return fail(FA_ERR_WORKSPACE, "zeroing the workspace failed on device %d", dev);
         }
         if (!blk) {
-            g_ws.push_back({dev, stream, nullptr, 0, 0});
+            g_ws.push_back({dev, stream, nullptr, 0, 0, 0});
             blk = &g_ws.back();
         }
         blk->ptr = static_cast<char*>(p);
         blk->cap_items = cap_items;
         blk->cap_parts = cap_parts;
+        blk->cap_o = cap_o;
     }
     ws->ctr = reinterpret_cast<int*>(blk->ptr);
     ws->lw = reinterpret_cast<float*>(blk->ptr + workspace_lw_offset(blk->cap_items));
@@ -696,46 +119,52 @@ int acquire_workspace(int dev, void* stream, long long items, long long parts, W
 namespace fa {
 namespace {
 
-// Both entry points: q_len queries at the last q_len of kv_len positions.
-int launch(const void* q, const void* k, const void* v, float* out, int n_q_heads, int n_kv_heads,
-           int q_len, int kv_len, int head_dim, float scale, int causal, void* stream) {
+// Every entry point: q_len queries at the last q_len of kv_len positions.
+int launch(const void* q, const void* k, const void* v, void* out, int n_q_heads, int n_kv_heads,
+           int q_len, int kv_len, int head_dim, float scale, int causal, int in_dtype, int out_dtype,
+           void* stream) {
     clear_error();
     fa_plan plan;
-    int st = make_plan(n_q_heads, n_kv_heads, q_len, kv_len, head_dim, causal, 0, 0, nullptr);
+    int st = check_dtypes(in_dtype, out_dtype);
     if (st != FA_OK) return st;
-    st = validate_call(q, k, v, out, n_q_heads, n_kv_heads, q_len, kv_len, head_dim, scale);
+    st = make_plan(n_q_heads, n_kv_heads, q_len, kv_len, head_dim, causal, 0, 0, nullptr);
+    if (st != FA_OK) return st;
+    st = validate_call(q, k, v, out, n_q_heads, n_kv_heads, q_len, kv_len, head_dim, scale,
+                       dtype_bytes(out_dtype));
     if (st != FA_OK) return st;
     if (q_len == 0) return FA_OK;
 
     int dev = -1, n_cus = 0;
+    long long max_lds = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(FA_ERR_DEVICE, "hipGetDevice failed");
-    st = check_device(dev, &n_cus);
+    st = check_device(dev, &n_cus, &max_lds);
     if (st != FA_OK) return st;
-    st = make_plan(n_q_heads, n_kv_heads, q_len, kv_len, head_dim, causal, 0, n_cus, &plan);
+    st = make_plan(n_q_heads, n_kv_heads, q_len, kv_len, head_dim, causal,
+                   (int)std::min<long long>(max_lds, 1 << 30), n_cus, &plan);
     if (st != FA_OK) return st;
     Workspace ws{nullptr, nullptr, nullptr};
     int n_splits = plan.kv_splits;
     if (n_splits > 1) {
         const long long items = (long long)plan.n_q_tiles * n_q_heads;
-        st = acquire_workspace(dev, stream, items, items * n_splits, &ws);
+        st = acquire_workspace(dev, stream, items, items * n_splits,
+                               items * n_splits * (long long)kQTile * head_dim, &ws);
         if (st != FA_OK) return st;
     }
 
     // Base-2 softmax: fold log2(e) into the scale.  A negative scale is
-    // applied as |scale| with Q negated (exact in f16), so the kernel's
+    // applied as |scale| with Q negated (exact: a sign flip), so the kernel's
     // running maximum is always taken over a positive multiple of s.  A zero
     // scale is applied as Q = 0 with multiplier 1 (every visible score 0),
     // which keeps masked scores at -inf * 1 rather than -inf * 0.
     int q_mode = scale < 0.0f ? 1 : (scale == 0.0f ? 2 : 0);
     float c2 = q_mode == 2 ? 1.0f : (float)(std::fabs((double)scale) * 1.4426950408889634);
-    const _Float16* qh = static_cast<const _Float16*>(q);
-    const _Float16* kh = static_cast<const _Float16*>(k);
-    const _Float16* vh = static_cast<const _Float16*>(v);
     int n_q_tiles = plan.n_q_tiles;
-    void* args[] = {&qh,    &kh,      &vh,     &out,    &q_len,  &kv_len,  &n_q_heads, &n_kv_heads,
-                    &n_q_tiles, &c2, &q_mode, &n_splits, &ws.ctr, &ws.lw, &ws.o};
-    const void* fn = causal ? reinterpret_cast<const void*>(&fa_prefill_kernel<true>)
-                            : reinterpret_cast<const void*>(&fa_prefill_kernel<false>);
+    void* args[] = {&q,         &k,  &v,      &out,     &q_len,  &kv_len, &n_q_heads, &n_kv_heads,
+                    &n_q_tiles, &c2, &q_mode, &n_splits, &ws.ctr, &ws.lw,  &ws.o};
+    const bool bf16 = in_dtype == FA_DTYPE_BF16, f32 = out_dtype == FA_DTYPE_F32;
+    const void* fn = head_dim == 64    ? prefill_kernel_hd64(bf16, f32, causal != 0)
+                     : head_dim == 128 ? prefill_kernel_hd128(bf16, f32, causal != 0)
+                                       : prefill_kernel_hd256(bf16, f32, causal != 0);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)plan.n_groups), dim3(kThreads), args, 0,
                                    static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "hipLaunchKernel: %s", hipGetErrorString(e));
@@ -749,7 +178,7 @@ extern "C" int fa_prefill(const void* q, const void* k, const void* v, float* ou
                           int n_kv_heads, int seq_len, int head_dim, float scale, int causal,
                           void* stream) {
     return fa::launch(q, k, v, out, n_q_heads, n_kv_heads, seq_len, seq_len, head_dim, scale, causal,
-                      stream);
+                      FA_DTYPE_F16, FA_DTYPE_F32, stream);
 }
 
 extern "C" int fa_prefill_free_workspaces(void) {
@@ -774,5 +203,12 @@ extern "C" int fa_prefill_chunk(const void* q, const void* k, const void* v, flo
                                 int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim,
                                 float scale, int causal, void* stream) {
     return fa::launch(q, k, v, out, n_q_heads, n_kv_heads, q_len, kv_len, head_dim, scale, causal,
-                      stream);
+                      FA_DTYPE_F16, FA_DTYPE_F32, stream);
+}
+
+extern "C" int fa_prefill_ex(const void* q, const void* k, const void* v, void* out, int n_q_heads,
+                             int n_kv_heads, int q_len, int kv_len, int head_dim, float scale,
+                             int causal, int in_dtype, int out_dtype, void* stream) {
+    return fa::launch(q, k, v, out, n_q_heads, n_kv_heads, q_len, kv_len, head_dim, scale, causal,
+                      in_dtype, out_dtype, stream);
 }

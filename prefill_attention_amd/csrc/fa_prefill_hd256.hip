@@ -1,0 +1,12 @@
+// Instantiations of the prefill attention kernel for head_dim 256: f16 or
+// bf16 inputs, f32 or input-type output, causal or full.
+#include "fa_internal.h"
+#include "fa_prefill_kernel.h"
+
+namespace fa {
+
+const void* prefill_kernel_hd256(bool in_bf16, bool out_f32, bool causal) {
+    return pick_kernel<256>(in_bf16, out_f32, causal);
+}
+
+}  // namespace fa

@@ -12,13 +12,15 @@ no activation statistics, so N(0, 1) draws rounded to f16 stand in for the
 projected Q/K/V activations at those shapes.
 
 Recipe (per workload, from one CPU generator seeded with ``seed``):
-    q = f16(randn([Q, n_q_heads, 128]))
-    k = f16(k_mult * randn([S, n_kv_heads, 128]))     (k_mult = 3 for the GQA case)
-    v = f16(randn([S, n_kv_heads, 128]))
-drawn in that order, S = ``seq_len`` keys and Q = ``q_len`` queries.  A
-full prefill has Q = S.  A chunked prefill (Q < S) is the last Q tokens of
-an S-token sequence whose first S - Q tokens are already in the KV cache: its
-queries sit at positions S - Q .. S - 1.  scale = float32(1 / sqrt(128)).
+    q = T(randn([Q, n_q_heads, D]))
+    k = T(k_mult * randn([S, n_kv_heads, D]))     (k_mult = 3 for the GQA case)
+    v = T(randn([S, n_kv_heads, D]))
+drawn in that order, S = ``seq_len`` keys, Q = ``q_len`` queries, D =
+``head_dim`` (128 unless stated), T = rounding to the input type (f16 unless
+stated; bf16 for the bf16 variants).  A full prefill has Q = S.  A chunked
+prefill (Q < S) is the last Q tokens of an S-token sequence whose first
+S - Q tokens are already in the KV cache: its queries sit at positions
+S - Q .. S - 1.  scale = float32(1 / sqrt(D)).
 
 The K/V producer's workloads (``STORE_WORKLOADS``) draw f32 K and V rows
 from N(0, 1), the activations the attention inputs above are rounded from,
@@ -53,6 +55,14 @@ class Workload:
     oracle_rows: int | None = None
     # queries (the last q_len positions of the sequence); None: a full prefill
     q_rows: int | None = None
+    # element types: inputs "f16" or "bf16"; output "f32" or the input type
+    in_dtype: str = "f16"
+    out_dtype: str = "f32"
+
+    @property
+    def scale(self) -> float:
+        """float32(1 / sqrt(head_dim))."""
+        return float(np.float32(1.0 / math.sqrt(self.head_dim)))
 
     @property
     def q_len(self) -> int:
@@ -81,8 +91,8 @@ class Workload:
             "seq_len": self.seq_len,
             "head_dim": self.head_dim,
             "causal": self.causal,
-            "dtype_in": "f16",
-            "dtype_out": "f32",
+            "dtype_in": self.in_dtype,
+            "dtype_out": self.out_dtype,
         }
         if self.chunked:
             d["q_len"] = self.q_len
@@ -111,31 +121,59 @@ WORKLOADS = {
         "chunk_16_8k", "7B-layer chunked causal prefill: 16 new tokens over an 8176-token KV cache, "
         "32/32 heads, hd=128", 32, 32, 8192, seed=7, q_rows=16,
     ),
+    # element-type and head-dimension variants at the 2659-token anchor (the
+    # same model width, n_heads x head_dim = 4096, for the other head sizes)
+    "7b_2659_bf16": Workload(
+        "7b_2659_bf16", "7B-layer causal prefill at the 2659-token anchor, bf16 in / f32 out, 32/32 heads, "
+        "hd=128", 32, 32, 2659, seed=3, in_dtype="bf16",
+    ),
+    "7b_2659_f16out": Workload(
+        "7b_2659_f16out", "7B-layer causal prefill at the 2659-token anchor, f16 in / f16 out, 32/32 heads, "
+        "hd=128", 32, 32, 2659, seed=3, out_dtype="f16",
+    ),
+    "7b_2659_bf16out": Workload(
+        "7b_2659_bf16out", "7B-layer causal prefill at the 2659-token anchor, bf16 in / bf16 out, 32/32 "
+        "heads, hd=128", 32, 32, 2659, seed=3, in_dtype="bf16", out_dtype="bf16",
+    ),
+    "hd64_2659": Workload(
+        "hd64_2659", "causal prefill at the 2659-token anchor, 64/64 heads, hd=64", 64, 64, 2659, seed=8,
+        head_dim=64,
+    ),
+    "hd256_2659": Workload(
+        "hd256_2659", "causal prefill at the 2659-token anchor, 16/16 heads, hd=256", 16, 16, 2659, seed=9,
+        head_dim=256,
+    ),
 }
 
 # Workload the throughput figure is quoted on.
 HEADLINE = "7b_2659"
 
 
+TORCH_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+
 def make_inputs(wl: Workload, seed: int | None = None, device: str = "cpu"):
-    """(q, k, v) f16 tensors: q [q_len, n_q_heads, hd], k/v [seq_len, n_kv_heads, hd],
-    drawn as described in the module docstring."""
+    """(q, k, v) tensors of the workload's input type (f16 or bf16): q
+    [q_len, n_q_heads, hd], k/v [seq_len, n_kv_heads, hd], drawn as described
+    in the module docstring."""
     g = torch.Generator(device="cpu").manual_seed(wl.seed if seed is None else seed)
     S, hd = wl.seq_len, wl.head_dim
-    q = torch.randn([wl.q_len, wl.n_q_heads, hd], dtype=torch.float32, generator=g).half()
-    k = (wl.k_mult * torch.randn([S, wl.n_kv_heads, hd], dtype=torch.float32, generator=g)).half()
-    v = torch.randn([S, wl.n_kv_heads, hd], dtype=torch.float32, generator=g).half()
+    dt = TORCH_DTYPES[wl.in_dtype]
+    q = torch.randn([wl.q_len, wl.n_q_heads, hd], dtype=torch.float32, generator=g).to(dt)
+    k = (wl.k_mult * torch.randn([S, wl.n_kv_heads, hd], dtype=torch.float32, generator=g)).to(dt)
+    v = torch.randn([S, wl.n_kv_heads, hd], dtype=torch.float32, generator=g).to(dt)
     if device != "cpu":
         q, k, v = q.to(device), k.to(device), v.to(device)
     return q, k, v
 
 
 def make_custom_inputs(seq_len: int, n_q_heads: int, n_kv_heads: int, seed: int,
-                       head_dim: int = HEAD_DIM, k_mult: float = 1.0, q_len: int | None = None):
+                       head_dim: int = HEAD_DIM, k_mult: float = 1.0, q_len: int | None = None,
+                       in_dtype: str = "f16"):
     """Same recipe at an arbitrary shape (tail sweeps, edge cases); ``q_len``
     queries at the last positions of a ``seq_len``-token sequence (default all)."""
     wl = Workload("custom", "custom", n_q_heads, n_kv_heads, seq_len, seed, k_mult=k_mult, head_dim=head_dim,
-                  q_rows=q_len)
+                  q_rows=q_len, in_dtype=in_dtype)
     return make_inputs(wl)
 
 

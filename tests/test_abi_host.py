@@ -56,8 +56,11 @@ def test_every_declared_symbol_exported():
 
 def test_status_codes_match_header():
     text = open(HEADER).read()
-    codes = dict((name, int(val)) for name, val in re.findall(r"(FA_\w+)\s*=\s*(\d+)", text))
+    codes = dict((name, int(val)) for name, val in re.findall(r"(FA_(?:OK|ERR_\w+))\s*=\s*(\d+)", text))
     assert codes == {v: k for k, v in STATUS_NAMES.items()}
+    dtypes = dict((name, int(val)) for name, val in re.findall(r"(FA_DTYPE_\w+)\s*=\s*(\d+)", text))
+    from prefill_attention_amd.binding import FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32
+    assert dtypes == {"FA_DTYPE_F16": FA_DTYPE_F16, "FA_DTYPE_BF16": FA_DTYPE_BF16, "FA_DTYPE_F32": FA_DTYPE_F32}
     for code in codes.values():
         assert fa.fa_prefill_strerror(code)
     assert "unknown" in fa.fa_prefill_strerror(99)
@@ -75,7 +78,7 @@ def call(**kw):
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(out=None), 1),
     (dict(seq_len=-1), 2), (dict(n_q_heads=0), 2), (dict(n_kv_heads=0), 2), (dict(n_q_heads=-4), 2),
     (dict(n_q_heads=6, n_kv_heads=4), 2), (dict(n_q_heads=2, n_kv_heads=4), 2),
-    (dict(head_dim=64), 3), (dict(head_dim=256), 3),
+    (dict(head_dim=96), 3), (dict(head_dim=0), 3), (dict(head_dim=512), 3), (dict(head_dim=-128), 3),
     (dict(scale=float("nan")), 4), (dict(scale=float("inf")), 4), (dict(scale=-float("inf")), 4),
     (dict(q=FAKE + 2), 5), (dict(k=FAKE + 0x100008), 5), (dict(out=FAKE + 0x400004), 5),
     (dict(out=FAKE), 8), (dict(out=FAKE + 0x200000 + 4096), 8),
@@ -91,18 +94,20 @@ def test_seq_len_zero_is_ok_without_gpu():
     assert call(seq_len=0, q=None, k=None, v=None, out=None) == 0
 
 
+@pytest.mark.parametrize("hd", [64, 128, 256])
 @pytest.mark.parametrize("S,nq,nkv,causal", [
     (256, 2, 2, 1), (2048, 32, 32, 1), (2659, 32, 32, 1), (4096, 32, 8, 1), (16384, 32, 8, 1),
     (1, 1, 1, 1), (129, 3, 1, 0), (0, 4, 4, 1), (2659, 32, 32, 0),
 ])
-def test_plan_geometry(S, nq, nkv, causal):
-    p = fa.fa_prefill_plan(nq, nkv, S, 128, causal)
+def test_plan_geometry(S, nq, nkv, causal, hd):
+    p = fa.fa_prefill_plan(nq, nkv, S, hd, causal)
     # the LDS request is exactly the sum of the planes the kernel lays out
     # (K and V stages, and a 16-byte merge flag)
     assert p.lds_bytes == p.lds_k_bytes + p.lds_v_bytes + 16
-    assert p.lds_k_bytes == p.stages * p.kv_tile * 128 * 2
-    assert p.lds_v_bytes == p.stages * p.kv_tile * 128 * 2
-    assert p.lds_bytes * (8 // p.waves_per_group) <= 160 * 1024  # 8 resident waves per CU fit 160 KiB
+    assert p.lds_k_bytes == p.stages * p.kv_tile * hd * 2
+    assert p.lds_v_bytes == p.stages * p.kv_tile * hd * 2
+    assert p.groups_per_cu == (1 if hd == 256 else 2)
+    assert p.lds_bytes * p.groups_per_cu <= 160 * 1024  # the resident work-groups fit 160 KiB
     assert p.threads_per_group == 64 * p.waves_per_group
     assert p.q_tile == 32 * p.waves_per_group
     assert p.n_q_tiles == math.ceil(S / p.q_tile)
@@ -148,7 +153,7 @@ def call_chunk(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(out=None), 1),
     (dict(q_len=-1), 2), (dict(kv_len=15), 2), (dict(q_len=16, kv_len=-1), 2),
-    (dict(n_q_heads=6, n_kv_heads=4), 2), (dict(head_dim=64), 3), (dict(scale=float("nan")), 4),
+    (dict(n_q_heads=6, n_kv_heads=4), 2), (dict(head_dim=48), 3), (dict(scale=float("nan")), 4),
     (dict(k=FAKE + 0x100004), 5),
     # out overlaps k, which is longer than q: [k, k + 48*2*256) covers k + 0x4000
     (dict(out=FAKE + 0x100000 + 0x4000), 8),
@@ -274,3 +279,59 @@ def test_store_binding_rejects_bad_tensors_without_gpu():
         fa.store_kv(k, k, pos, kc, kc)  # CPU tensors
     with pytest.raises(ValueError):
         fa.convert_f16(k)  # CPU tensor
+
+
+# ------------------------------------------------------ element-type variants
+def call_ex(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, out=FAKE + 0x400000, n_q_heads=4,
+             n_kv_heads=2, q_len=16, kv_len=16, head_dim=128, scale=0.088, causal=1, in_dtype=0,
+             out_dtype=2, stream=None)
+    a.update(kw)
+    return fa.fa_prefill_ex(a["q"], a["k"], a["v"], a["out"], a["n_q_heads"], a["n_kv_heads"], a["q_len"],
+                            a["kv_len"], a["head_dim"], a["scale"], a["causal"], a["in_dtype"],
+                            a["out_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(in_dtype=2), 11), (dict(in_dtype=3), 11), (dict(in_dtype=-1), 11), (dict(out_dtype=3), 11),
+    (dict(in_dtype=0, out_dtype=1), 11), (dict(in_dtype=1, out_dtype=0), 11),
+    (dict(head_dim=32), 3), (dict(q=None), 1), (dict(kv_len=8), 2),
+    # an f32 output of 16 x 4 x 128 overlaps v 2 MiB below it; a 16-bit one ends before it
+    (dict(out=FAKE + 0x200000 - 16 * 4 * 128 * 4 + 16, out_dtype=2), 8),
+    (dict(out=FAKE + 0x200000 - 16 * 4 * 128 * 2 + 16, in_dtype=1, out_dtype=1), 8),
+])
+def test_ex_argument_errors(kw, code):
+    st = call_ex(**kw)
+    assert st == code, (kw, st, fa.fa_prefill_last_error())
+    assert fa.fa_prefill_last_error()
+
+
+@pytest.mark.parametrize("in_dtype,out_dtype", [(0, 2), (0, 0), (1, 2), (1, 1)])
+def test_ex_supported_dtypes_pass_validation(in_dtype, out_dtype):
+    # valid combinations reach the device check (FA_ERR_DEVICE here, without a GPU)
+    st = call_ex(in_dtype=in_dtype, out_dtype=out_dtype)
+    assert st in (0, 9), (st, fa.fa_prefill_last_error())
+    # a 16-bit output directly below v is not an alias when it ends there
+    st = call_ex(in_dtype=in_dtype, out_dtype=out_dtype,
+                 out=FAKE + 0x200000 - 16 * 4 * 128 * (4 if out_dtype == 2 else 2))
+    assert st in (0, 9), (st, fa.fa_prefill_last_error())
+
+
+def test_ex_q_len_zero_is_ok_without_gpu():
+    assert call_ex(q_len=0, q=None, k=None, v=None, out=None, in_dtype=1, out_dtype=1) == 0
+
+
+def test_chunk_plan_splits_head_dim_256_fewer_slots():
+    # one resident work-group per CU halves the slots a split may fill
+    p128 = fa.fa_prefill_chunk_plan(32, 32, 16, 8192, 128, 1)
+    p256 = fa.fa_prefill_chunk_plan(32, 32, 16, 8192, 256, 1)
+    assert p128.kv_splits == 8 and p256.kv_splits == 8
+    p128 = fa.fa_prefill_chunk_plan(32, 32, 256, 8192, 128, 1)
+    p256 = fa.fa_prefill_chunk_plan(32, 32, 256, 8192, 256, 1)
+    assert p128.kv_splits == 8 and p256.kv_splits == 4
+    # partial outputs are [parts][128][head_dim] f32 after the counters and log-weights
+    items = 2 * 32
+    lw_off = ((items * 4 + 255) // 256) * 256
+    for p, hd in ((p128, 128), (p256, 256)):
+        parts = items * p.kv_splits
+        assert p.workspace_bytes == lw_off + parts * 128 * 4 + parts * 128 * hd * 4

@@ -107,12 +107,17 @@ def pin_golden():
 
 
 def pin_library():
-    """torch SDPA float64: MHA causal / full at the tiny workload, GQA causal / full."""
+    """torch SDPA float64: MHA causal / full at the tiny workload, GQA causal / full,
+    head_dim 64 and 256, and bf16 inputs (widened exactly)."""
     fails = []
     wl = WORKLOADS["tiny"]
     q, k, v = make_inputs(wl)
     q8, k8, v8 = make_custom_inputs(48, 8, 2, seed=7)
-    for tag, (a, b, c) in (("mha", (q, k, v)), ("gqa", (q8, k8, v8))):
+    cases = [("mha", (q, k, v)), ("gqa", (q8, k8, v8)),
+             ("hd64", make_custom_inputs(40, 4, 2, seed=17, head_dim=64)),
+             ("hd256", make_custom_inputs(40, 2, 1, seed=18, head_dim=256)),
+             ("bf16", make_custom_inputs(40, 4, 4, seed=19, in_dtype="bf16"))]
+    for tag, (a, b, c) in cases:
         for causal in (True, False):
             try:
                 got = attention_f64(a, b, c, SCALE, causal)
@@ -339,6 +344,20 @@ def test_parity_metric():
     assert not within_tolerance(e)
     assert within_tolerance(parity_errors(ref + 1e-3, ref))
     assert not within_tolerance(parity_errors(np.array([np.nan, 0, 0, 0]), ref))
+
+
+def test_parity_metric_out_unit_and_bars():
+    from oracle import OUT_UNIT, bar
+
+    ref = np.array([0.5, -2.0, 3.0, 0.0])
+    # rounding to f16 alone is forgiven exactly, nothing more
+    g16 = ref.astype(np.float16).astype(np.float64)
+    assert parity_errors(g16, ref, OUT_UNIT["f16"])["max_abs"] == 0.0
+    near = np.array([0.5 + 1e-3, -2.0, 3.0, 0.0])
+    e = parity_errors(near, ref, OUT_UNIT["f16"])
+    assert math.isclose(e["max_abs"], 1e-3 - 0.5 * 2.0 ** -11, rel_tol=1e-9)
+    assert bar("f16") == (2e-3, 1e-2) and bar("bf16") == (1.6e-2, 8e-2)
+    assert OUT_UNIT["bf16"] == 8 * OUT_UNIT["f16"]
 
 
 # ------------------------------------------------------------- mutation harness
