@@ -335,3 +335,26 @@ def test_chunk_plan_splits_head_dim_256_fewer_slots():
     for p, hd in ((p128, 128), (p256, 256)):
         parts = items * p.kv_splits
         assert p.workspace_bytes == lw_off + parts * 128 * 4 + parts * 128 * hd * 4
+
+
+def test_committed_traffic_records_match_the_kernels():
+    """profiles/*_traffic.json were taken on the committed kernel sources, so
+    bench.py reports their HBM bytes (and the records are self-consistent)."""
+    import json
+    import sys
+
+    sys.path.insert(0, ROOT)
+    import bench
+
+    att = json.load(open(os.path.join(ROOT, "profiles", "fa_prefill_kernel_traffic.json")))
+    assert att["kernel_source_hash"] == bench.kernel_source_hash(), "re-profile the attention kernel"
+    assert bench.measured_traffic("7b_2659") == att["hbm_bytes_per_launch"]
+    cal = att["calibration"]
+    assert abs(att["fetch_size_kib_per_launch"] * 1024 * cal["fetch_scale"]
+               + att["write_size_kib_per_launch"] * 1024 * cal["write_scale"] - att["hbm_bytes_per_launch"]) < 4096
+    st = json.load(open(os.path.join(ROOT, "profiles", "fa_store_kv_traffic.json")))
+    assert st["kernel_source_hash"] == bench.kernel_source_hash(bench.STORE_SOURCES), "re-profile the K/V producer"
+    assert bench.measured_traffic("kv_store_2659", bench.STORE_TRAFFIC_FILE, bench.STORE_SOURCES) == st["hbm_bytes_per_launch"]
+    from prefill_attention_amd.workloads import STORE_WORKLOADS
+
+    assert st["algorithmic_bytes_per_launch"] == STORE_WORKLOADS["kv_store_2659"].algorithmic_bytes
