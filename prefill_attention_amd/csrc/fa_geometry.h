@@ -30,7 +30,7 @@ constexpr int groups_per_cu(int hd) { return hd > 128 ? 1 : 2; }
 // a long KV cache): each query tile's key range is divided over up to
 // kMaxSplits work-groups, each part at least kMinSplitTiles key tiles long.
 constexpr int kMaxSplits = 8;
-constexpr int kMinSplitTiles = 4;
+constexpr int kMinSplitTiles = 20;
 
 // LDS planes.  K and V tiles are both stored key-major with unpadded rows of
 // head_dim 16-bit elements; the 16-byte chunks of a row are permuted by

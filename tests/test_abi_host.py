@@ -189,11 +189,12 @@ def workspace_bytes(items, parts, q_tile=128):
 
 
 @pytest.mark.parametrize("nq,q_len,kv_len,causal,splits", [
-    (32, 512, 4096, 1, 4),    # 128 tiles on 512 slots, 56 shared key tiles: 4 parts
-    (32, 1, 4096, 1, 8),      # one new token: capped at 8 parts
-    (32, 1, 200, 1, 1),       # cache too short for parts of >= 4 key tiles
+    (32, 512, 4096, 1, 2),    # 128 tiles on 512 slots, 57 shared key tiles: 2 parts of >= 20
+    (32, 1, 4096, 1, 3),      # one new token, 64 shared key tiles: 3 parts
+    (32, 1, 16384, 1, 8),     # one new token over 16K keys: capped at 8 parts
+    (32, 1, 1200, 1, 1),      # cache too short for two parts of >= 20 key tiles
     (32, 2048, 4096, 1, 1),   # 512 tiles already fill the slots
-    (8, 256, 8192, 0, 8),     # non-causal: every key is shared
+    (8, 256, 8192, 0, 6),     # non-causal: every key is shared (128 tiles)
     (6, 1, 4096, 1, 1),       # head count not a multiple of 8: never split
 ])
 def test_chunk_plan_splits(nq, q_len, kv_len, causal, splits):
@@ -325,10 +326,10 @@ def test_chunk_plan_splits_head_dim_256_fewer_slots():
     # one resident work-group per CU halves the slots a split may fill
     p128 = fa.fa_prefill_chunk_plan(32, 32, 16, 8192, 128, 1)
     p256 = fa.fa_prefill_chunk_plan(32, 32, 16, 8192, 256, 1)
-    assert p128.kv_splits == 8 and p256.kv_splits == 8
+    assert p128.kv_splits == 6 and p256.kv_splits == 6
     p128 = fa.fa_prefill_chunk_plan(32, 32, 256, 8192, 128, 1)
     p256 = fa.fa_prefill_chunk_plan(32, 32, 256, 8192, 256, 1)
-    assert p128.kv_splits == 8 and p256.kv_splits == 4
+    assert p128.kv_splits == 6 and p256.kv_splits == 4
     # partial outputs are [parts][128][head_dim] f32 after the counters and log-weights
     items = 2 * 32
     lw_off = ((items * 4 + 255) // 256) * 256

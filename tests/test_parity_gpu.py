@@ -293,9 +293,9 @@ def _chunk_plan(fa, nq, nkv, q_len, kv_len, causal=True):
 
 
 @pytest.mark.parametrize("q_len,kv_len,heads,causal", [
-    (1, 4096, (8, 2), True), (1, 600, (8, 8), True), (3, 1000, (16, 4), True),
-    (37, 3000, (8, 8), True), (129, 2051, (8, 1), True), (200, 5000, (16, 4), True),
-    (64, 700, (8, 8), False), (1, 2049, (32, 8), False),
+    (1, 4096, (8, 2), True), (1, 2600, (8, 8), True), (3, 3000, (16, 4), True),
+    (37, 3000, (8, 8), True), (129, 3100, (8, 1), True), (200, 5000, (16, 4), True),
+    (64, 2700, (8, 8), False), (1, 2600, (32, 8), False), (1, 11000, (8, 8), True),
 ])
 def test_split_kv_parity(fa, q_len, kv_len, heads, causal):
     nq, nkv = heads
@@ -327,7 +327,7 @@ def test_split_kv_deterministic_and_peaked(fa):
 
 def test_split_kv_workspace_reuse_growth_and_streams(fa):
     # shapes needing different workspace sizes, alternated on two streams
-    shapes = [(1, 2000, 8, 2), (128, 6000, 16, 4), (1, 2000, 8, 2), (40, 3000, 8, 8)]
+    shapes = [(1, 2700, 8, 2), (128, 6000, 16, 4), (1, 2700, 8, 2), (40, 3000, 8, 8)]
     cases = []
     for i, (Q, S, nq, nkv) in enumerate(shapes):
         assert _chunk_plan(fa, nq, nkv, Q, S).kv_splits > 1
