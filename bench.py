@@ -229,7 +229,7 @@ def main() -> int:
     import torch
 
     import prefill_attention_amd as fa
-    from prefill_attention_amd.workloads import HEADLINE, SCALE, WORKLOADS, make_inputs
+    from prefill_attention_amd.workloads import HEADLINE, WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
