@@ -26,7 +26,7 @@ stored sequence ("28 · r23 — f16-path whole-graph wall decomposition",
 §2.3 and the mask excerpt in §3.2).  Without ``causal`` every key of the
 sequence is visible.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 * grouped-query mapping: consecutive groups, hk = h // (n_q_heads // n_kv_heads);
 * a full prefill's query positions equal key positions 0..S-1; a chunk of Q
   new tokens over a cache of S - Q tokens has queries at S - Q .. S - 1

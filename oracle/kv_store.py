@@ -21,7 +21,7 @@ a magnitude of at least 65520 (halfway between the largest finite value,
 65504, and the next power-of-two step, 65536) to infinity, a NaN to a NaN,
 with the sign kept (so negative values that round to zero give -0).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 * "round to nearest" is round-to-nearest-even, IEEE 754's default and the
   rounding of the ``_rn`` conversion named on the page;
 * positions are distinct and inside the cache; a position outside the cache
