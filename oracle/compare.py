@@ -19,7 +19,7 @@ ATOL = 2e-3
 RTOL = 1e-2
 REL_FLOOR = ATOL / RTOL  # 0.2
 
-# Other element types, derived from the f16 bar (see DESIGN):
+# Other element types, derived from the f16 bar:
 # * bf16 inputs: the probabilities enter P.V rounded to bf16, whose unit
 #   roundoff (2^-8) is 8 times f16's (2^-11); the error the bar allows for
 #   that rounding scales with it, so the bar is 8 x (ATOL, RTOL).
