@@ -111,7 +111,10 @@ typedef struct fa_plan {
     int kv_splits;           /* work-groups sharing one query tile's key range
                                 (split-KV; 1 = no split)                          */
     int n_q_tiles;           /* ceil(q_len / q_tile)                              */
-    long long n_groups;      /* work-groups launched: n_q_tiles * n_q_heads * kv_splits */
+    long long n_groups;      /* work-groups launched: n_q_tiles * n_q_heads * kv_splits,
+                                the item count n_q_tiles * n_q_heads rounded up to a
+                                multiple of 8 for a split launch whose n_q_heads is
+                                not a multiple of 8 (padding work-groups exit at once) */
     int stages;              /* K/V tiles resident in LDS                          */
     int lds_bytes;           /* LDS per work-group: the sum of its planes (K, V and
                                 a 16-byte flag)                                    */

@@ -64,12 +64,12 @@ int check_dtypes(int in_dtype, int out_dtype) {
 // in every part (the parts share out the tiles that start at or before that
 // position; the last part also takes the diagonal and tail tiles): with the
 // causal mask this needs a KV cache in front of the chunk.  All parts of a
-// tile must run on one XCD (they meet through its L2), which the XCD-wise
-// head assignment guarantees when the head count is a multiple of 8.
-static int choose_splits(long long items, long long q_off, long long kv_len, bool causal, int n_q_heads,
-                         int n_cus, int head_dim) {
+// tile run on one XCD (they meet through its L2); the kernel's work-group
+// mapping guarantees it for every head count.
+static int choose_splits(long long items, long long q_off, long long kv_len, bool causal, int n_cus,
+                         int head_dim) {
     const long long slots = (long long)groups_per_cu(head_dim) * n_cus;
-    if (items <= 0 || items * 2 > slots || n_q_heads % kXcds != 0) return 1;
+    if (items <= 0 || items * 2 > slots) return 1;
     // tiles shared out, for the tile with the fewest (the first query tile)
     const long long shared = causal ? q_off / kKvTile + 1 : (kv_len + kKvTile - 1) / kKvTile;
     long long n = slots / items;
@@ -108,10 +108,13 @@ int make_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim
                     lds_bytes(head_dim), max_lds_bytes);
     if (n_cus <= 0) n_cus = 256;
     const long long items = n_q_tiles * (long long)n_q_heads;
-    const int splits = choose_splits(items, (long long)kv_len - q_len, kv_len, causal != 0, n_q_heads, n_cus,
-                                     head_dim);
-    if (items * splits > INT_MAX)
-        return fail(FA_ERR_SHAPE, "grid of %lld work-groups exceeds the launch limit", items * splits);
+    const int splits = choose_splits(items, (long long)kv_len - q_len, kv_len, causal != 0, n_cus, head_dim);
+    // A split launch whose head count is not a multiple of 8 pads the items
+    // to a multiple of 8 (see the kernel's work-group mapping).
+    const long long grid_items =
+        splits == 1 || n_q_heads % kXcds == 0 ? items : (items + kXcds - 1) / kXcds * kXcds;
+    if (grid_items * splits > INT_MAX)
+        return fail(FA_ERR_SHAPE, "grid of %lld work-groups exceeds the launch limit", grid_items * splits);
     if (plan) {
         plan->q_tile = kQTile;
         plan->kv_tile = kKvTile;
@@ -119,7 +122,7 @@ int make_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim
         plan->threads_per_group = kThreads;
         plan->kv_splits = splits;
         plan->n_q_tiles = (int)n_q_tiles;
-        plan->n_groups = items * splits;
+        plan->n_groups = grid_items * splits;
         plan->workspace_bytes =
             splits > 1 ? workspace_bytes(items, items * splits, items * splits * (long long)kQTile * head_dim) : 0;
         plan->stages = kStages;

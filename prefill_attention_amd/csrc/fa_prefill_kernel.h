@@ -468,11 +468,14 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     const int l32 = lane & 31;
     const int g = lane >> 5;
 
-    // Work-group -> (head, query tile, key-range part): heaviest query tiles
-    // first; with a head count divisible by the XCD count, XCD x (= blockIdx
-    // % 8) owns heads [x*H/8, (x+1)*H/8), so one kv head's K/V stays in one
-    // L2 and all parts of a split query tile meet in that L2.  (Other head
-    // counts are never split.)
+    // Work-group -> (head, query tile, key-range part), heaviest query tiles
+    // first.  Work-groups are dispatched round-robin over the XCDs (XCD x =
+    // blockIdx % 8), and all parts of a split query tile must meet in one
+    // XCD's L2.  With a head count divisible by 8, XCD x owns heads
+    // [x*H/8, (x+1)*H/8), so one kv head's K/V also stays in one L2.  Other
+    // head counts deal the items (rank * H + head, heaviest first) round-robin
+    // over the XCDs, the parts of item i on XCD i % 8; the grid is padded to a
+    // multiple of 8 items, and padding work-groups exit at once.
     const int b = blockIdx.x;
     int h, rank, split = 0;
     if ((n_q_heads % kXcds) == 0) {
@@ -483,8 +486,12 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
         split = rem / per_xcd;
         h = (b % kXcds) * per_xcd + rem % per_xcd;
     } else {
-        h = b % n_q_heads;
-        rank = b / n_q_heads;
+        const int local = b / kXcds;
+        split = local % n_splits;
+        const int item = (local / n_splits) * kXcds + b % kXcds;
+        if (item >= n_q_tiles * n_q_heads) return;  // padding (uniform per work-group)
+        h = item % n_q_heads;
+        rank = item / n_q_heads;
     }
     const int qt = CAUSAL ? n_q_tiles - 1 - rank : rank;
     const int hk = h / (n_q_heads / n_kv_heads);

@@ -121,6 +121,10 @@ WORKLOADS = {
         "chunk_16_8k", "7B-layer chunked causal prefill: 16 new tokens over an 8176-token KV cache, "
         "32/32 heads, hd=128", 32, 32, 8192, seed=7, q_rows=16,
     ),
+    "chunk_16_8k_gqa28": Workload(
+        "chunk_16_8k_gqa28", "chunked causal prefill, 28 q / 4 kv heads (a 7B GQA layout with 4 kv heads): "
+        "16 new tokens over an 8176-token KV cache, hd=128", 28, 4, 8192, seed=10, q_rows=16,
+    ),
     # element-type and head-dimension variants at the 2659-token anchor (the
     # same model width, n_heads x head_dim = 4096, for the other head sizes)
     "7b_2659_bf16": Workload(

@@ -195,13 +195,15 @@ def workspace_bytes(items, parts, q_tile=128):
     (32, 1, 1200, 1, 1),      # cache too short for two parts of >= 20 key tiles
     (32, 2048, 4096, 1, 1),   # 512 tiles already fill the slots
     (8, 256, 8192, 0, 6),     # non-causal: every key is shared (128 tiles)
-    (6, 1, 4096, 1, 1),       # head count not a multiple of 8: never split
+    (6, 1, 4096, 1, 3),       # head count not a multiple of 8: items padded to 8
+    (28, 16, 8192, 1, 6),     # 28 query heads (4 kv heads): 28 items padded to 32
 ])
 def test_chunk_plan_splits(nq, q_len, kv_len, causal, splits):
     p = fa.fa_prefill_chunk_plan(nq, nq // 2 if nq % 2 == 0 else nq, q_len, kv_len, 128, causal)
     assert p.kv_splits == splits
     items = p.n_q_tiles * nq
-    assert p.n_groups == items * splits
+    grid_items = items if splits == 1 or nq % 8 == 0 else -(-items // 8) * 8
+    assert p.n_groups == grid_items * splits
     assert p.workspace_bytes == (workspace_bytes(items, items * splits) if splits > 1 else 0)
 
 

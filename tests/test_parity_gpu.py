@@ -308,6 +308,24 @@ def test_split_kv_parity(fa, q_len, kv_len, heads, causal):
     assert within_tolerance(err), err
 
 
+@pytest.mark.parametrize("q_len,kv_len,heads", [
+    (16, 8192, (28, 4)), (1, 5000, (4, 4)), (130, 6000, (12, 4)), (1, 4096, (1, 1)), (77, 3500, (6, 2)),
+])
+def test_split_kv_any_head_count(fa, q_len, kv_len, heads):
+    """Head counts that are not a multiple of 8 split too: items dealt round-robin
+    over the XCDs, padded to a multiple of 8 work-groups."""
+    nq, nkv = heads
+    plan = _chunk_plan(fa, nq, nkv, q_len, kv_len)
+    assert plan.kv_splits > 1 and plan.n_groups % 8 == 0
+    q, k, v = make_custom_inputs(kv_len, nq, nkv, seed=q_len + kv_len + nq, q_len=q_len)
+    got = _run_chunk(fa, q, k, v)
+    err = parity_errors(got, attention_chunk_f64(q, k, v, SCALE, True))
+    _report(f"split q={q_len} kv={kv_len} heads={heads} parts={plan.kv_splits}", err)
+    assert within_tolerance(err), err
+    again = _run_chunk(fa, q, k, v)
+    assert np.array_equal(got, again), "merge depends on arrival order"
+
+
 def test_split_kv_deterministic_and_peaked(fa):
     # parts whose softmax masses differ by many powers of two (keys of the
     # newest quarter scaled up), merged in part order: identical on reruns
@@ -356,3 +374,13 @@ def test_split_kv_workspace_reuse_growth_and_streams(fa):
     again = fa.attention(dq, dk, dv, SCALE, True)   # allocates again after the release
     torch.cuda.synchronize()
     assert torch.equal(again, first[0])
+
+
+def test_chunk_gqa28_workload_full(fa):
+    wl = WORKLOADS["chunk_16_8k_gqa28"]
+    q, k, v = make_inputs(wl)
+    assert fa.fa_prefill_chunk_plan(wl.n_q_heads, wl.n_kv_heads, wl.q_len, wl.seq_len, 128, 1).kv_splits > 1
+    got = _run_chunk(fa, q, k, v)
+    err = parity_errors(got, attention_chunk_f64(q, k, v, SCALE, True))
+    _report(wl.key, err)
+    assert within_tolerance(err), err

@@ -57,7 +57,9 @@ def test_random_case(fa, case):
            f"causal={causal} scale={scale:.4g} K x{k_mult:g}")
     print(f"[random] {tag}", flush=True)
     plan = fa.fa_prefill_chunk_plan(nq, nkv, q_len, kv_len, hd, int(causal))
-    assert plan.n_q_tiles == -(-q_len // 128) and plan.n_groups == plan.n_q_tiles * nq * plan.kv_splits
+    items = plan.n_q_tiles * nq
+    grid_items = items if plan.kv_splits == 1 or nq % 8 == 0 else -(-items // 8) * 8
+    assert plan.n_q_tiles == -(-q_len // 128) and plan.n_groups == grid_items * plan.kv_splits
     q, k, v = make_custom_inputs(kv_len, nq, nkv, seed=1000 + i, head_dim=hd, k_mult=k_mult, q_len=q_len,
                                  in_dtype=in_dt)
     out = fa.attention(q.cuda(), k.cuda(), v.cuda(), scale, causal, out_dtype=TORCH_DTYPES[out_dt])
