@@ -55,6 +55,7 @@ class FaPlan(ctypes.Structure):
         ("kv_tiles_visited", ctypes.c_longlong),
         ("workspace_bytes", ctypes.c_longlong),
         ("groups_per_cu", ctypes.c_int),
+        ("phase_priority", ctypes.c_int),
     ]
 
     def as_dict(self) -> dict:

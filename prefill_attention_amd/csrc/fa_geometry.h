@@ -32,6 +32,10 @@ constexpr int groups_per_cu(int hd) { return hd > 128 ? 1 : 2; }
 constexpr int kMaxSplits = 8;
 constexpr int kMinSplitTiles = 20;
 
+// Phase-A issue priority is used when the heaviest work-group carries at most
+// this many times the average key tiles per resident work-group slot.
+constexpr double kPriorityMaxImbalance = 1.25;
+
 // LDS planes.  K and V tiles are both stored key-major with unpadded rows of
 // head_dim 16-bit elements; the 16-byte chunks of a row are permuted by
 // chunk ^ swizzle(row) (see the kernel), which keeps both the K operand

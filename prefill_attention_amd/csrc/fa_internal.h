@@ -36,12 +36,13 @@ int check_device(int dev, int* n_cus, long long* max_lds);
 int check_dtypes(int in_dtype, int out_dtype);
 inline int dtype_bytes(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
 
-// Kernel entry of one (head_dim, input type, output type, causal) variant
-// (fa_prefill_hd64/128/256.hip): in_bf16 selects bf16 inputs, out_f32 an
-// f32 output (else the input type).
-const void* prefill_kernel_hd64(bool in_bf16, bool out_f32, bool causal);
-const void* prefill_kernel_hd128(bool in_bf16, bool out_f32, bool causal);
-const void* prefill_kernel_hd256(bool in_bf16, bool out_f32, bool causal);
+// Kernel entry of one (head_dim, input type, output type, causal, phase
+// priority) variant (fa_prefill_hd64/128/256.hip): in_bf16 selects bf16
+// inputs, out_f32 an f32 output (else the input type), prio the instantiation
+// that raises issue priority in phase A (fa_plan.phase_priority).
+const void* prefill_kernel_hd64(bool in_bf16, bool out_f32, bool causal, bool prio);
+const void* prefill_kernel_hd128(bool in_bf16, bool out_f32, bool causal, bool prio);
+const void* prefill_kernel_hd256(bool in_bf16, bool out_f32, bool causal, bool prio);
 
 // Argument checks of the K/V producer's entry points (host only).
 int validate_store_kv(const float* k_new, const float* v_new, const int* positions, int n_tokens,

@@ -78,6 +78,20 @@ static int choose_splits(long long items, long long q_off, long long kv_len, boo
     return n >= 2 ? (int)n : 1;
 }
 
+// Phase-A issue priority (the kernel's prio_a): on when the launch is
+// throughput-bound, i.e. its heaviest work-group has at most
+// kPriorityMaxImbalance times the average key tiles per occupied slot (a
+// grid smaller than the resident slots occupies one slot per work-group);
+// off when one heavy query tile would set the kernel's length (a short
+// causal prefill), where the default arbitration, which runs the older and
+// heavier work-group first, measured faster.
+static int choose_phase_priority(long long max_group_tiles, long long total_tiles, long long n_groups,
+                                 long long slots) {
+    if (total_tiles <= 0 || n_groups <= 0) return 0;
+    const long long occupied = n_groups < slots ? n_groups : slots;
+    return (double)max_group_tiles * (double)occupied <= kPriorityMaxImbalance * (double)total_tiles ? 1 : 0;
+}
+
 int make_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim, int causal,
               int max_lds_bytes, int n_cus, fa_plan* plan) {
     if (q_len < 0) return fail(FA_ERR_SHAPE, "q_len %d < 0", q_len);
@@ -130,10 +144,17 @@ int make_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim
         plan->lds_k_bytes = lds_k_bytes(head_dim);
         plan->lds_v_bytes = lds_v_bytes(head_dim);
         plan->groups_per_cu = groups_per_cu(head_dim);
-        long long tiles = 0;
-        for (long long t = 0; t < n_q_tiles; ++t)
-            tiles += tiles_for_group(t * kQTile, (long long)kv_len - q_len, kv_len, causal != 0);
+        long long tiles = 0, max_tiles = 0;
+        for (long long t = 0; t < n_q_tiles; ++t) {
+            const long long n = tiles_for_group(t * kQTile, (long long)kv_len - q_len, kv_len, causal != 0);
+            tiles += n;
+            max_tiles = n > max_tiles ? n : max_tiles;
+        }
         plan->kv_tiles_visited = tiles * n_q_heads;
+        // a split tile's heaviest part: its share of the tiles plus the rest
+        const long long max_group_tiles = (max_tiles + splits - 1) / splits;
+        plan->phase_priority = choose_phase_priority(max_group_tiles, tiles * n_q_heads, plan->n_groups,
+                                                     (long long)groups_per_cu(head_dim) * n_cus);
     }
     return FA_OK;
 }

@@ -159,12 +159,19 @@ int launch(const void* q, const void* k, const void* v, void* out, int n_q_heads
     int q_mode = scale < 0.0f ? 1 : (scale == 0.0f ? 2 : 0);
     float c2 = q_mode == 2 ? 1.0f : (float)(std::fabs((double)scale) * 1.4426950408889634);
     int n_q_tiles = plan.n_q_tiles;
-    void* args[] = {&q,         &k,  &v,      &out,     &q_len,  &kv_len, &n_q_heads, &n_kv_heads,
-                    &n_q_tiles, &c2, &q_mode, &n_splits, &ws.ctr, &ws.lw,  &ws.o};
+    // Heavy-light pairing of the first dispatch wave: a causal, unsplit launch
+    // with two work-groups per CU whose heads divide over the XCDs.
+    int pair_span = (causal && n_splits == 1 && plan.groups_per_cu == 2 && n_q_heads % kXcds == 0 &&
+                     n_cus % kXcds == 0)
+                        ? n_cus / kXcds
+                        : 0;
+    void* args[] = {&q,         &k,  &v,      &out,     &q_len,     &kv_len, &n_q_heads, &n_kv_heads,
+                    &n_q_tiles, &c2, &q_mode, &n_splits, &pair_span, &ws.ctr, &ws.lw,     &ws.o};
     const bool bf16 = in_dtype == FA_DTYPE_BF16, f32 = out_dtype == FA_DTYPE_F32;
-    const void* fn = head_dim == 64    ? prefill_kernel_hd64(bf16, f32, causal != 0)
-                     : head_dim == 128 ? prefill_kernel_hd128(bf16, f32, causal != 0)
-                                       : prefill_kernel_hd256(bf16, f32, causal != 0);
+    const bool prio = plan.phase_priority != 0;
+    const void* fn = head_dim == 64    ? prefill_kernel_hd64(bf16, f32, causal != 0, prio)
+                     : head_dim == 128 ? prefill_kernel_hd128(bf16, f32, causal != 0, prio)
+                                       : prefill_kernel_hd256(bf16, f32, causal != 0, prio);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)plan.n_groups), dim3(kThreads), args, 0,
                                    static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "hipLaunchKernel: %s", hipGetErrorString(e));

@@ -63,7 +63,9 @@
 //
 //  * Work-group order: the heaviest query tiles first; when the head count is
 //    a multiple of 8, the 8 XCDs (which receive work-groups round-robin) each
-//    own a contiguous range of heads, so one kv head's K/V stays in one L2.
+//    own a contiguous range of heads, so one kv head's K/V stays in one L2,
+//    and an unsplit causal launch reverses the second half of each XCD's
+//    first dispatch wave so that heavy and light query tiles share CUs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -185,22 +187,22 @@ __device__ __forceinline__ int acc_key(int kb, int i, int g) {
     return 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
 }
 
-// Copy key/value rows [kt, kt + 64) of head hk from src ([kv_len][n_kv][HD],
-// 16-bit) into an LDS tile; this wavefront copies rows 16*wave .. 16*wave +
-// 15, 1 KiB per instruction.  Lane i of an instruction fills physical chunk
-// i % kChunks of its row, so it loads logical chunk (i % kChunks) ^ swz(row).
+// Copy key/value rows [kt, kt + 64) of head hk into an LDS tile; head_base
+// points at row 0 of head hk in src ([kv_len][n_kv][HD], 16-bit).  This
+// wavefront copies rows 16*wave .. 16*wave + 15, 1 KiB per instruction.
+// Lane i of an instruction fills physical chunk i % kChunks of its row, so it
+// loads logical chunk (i % kChunks) ^ swz(row).  The buffer record ends at
+// the last valid row of this head, so rows >= kv_len read as 0; the record
+// size is formed in 32 bits from the rows left (at least one).
 template <int HD>
-__device__ __forceinline__ void stage_tile(const void* __restrict__ src, int n_kv, int hk, int kv_len,
+__device__ __forceinline__ void stage_tile(const char* head_base, uint32_t row_bytes, int hk, int kv_len,
                                            int kt, char* tile, int wave, int lane) {
     using L = Tile<HD>;
-    const uint32_t row_bytes = (uint32_t)n_kv * L::kRowBytes;
-    const char* base = reinterpret_cast<const char*>(src) + (size_t)kt * row_bytes +
-                       (size_t)hk * L::kRowBytes;
-    // Bytes addressable from base: up to the end of the last valid row of
-    // this head, so rows >= kv_len fall outside the record and read as 0.
-    const long long valid = (long long)(kv_len - kt) * row_bytes - (long long)hk * L::kRowBytes;
-    const long long cap = (long long)kKvTile * row_bytes;
-    const uint32_t n_records = (uint32_t)(valid < cap ? valid : cap);
+    const char* base = head_base + (uint64_t)(uint32_t)kt * row_bytes;
+    const int rows_left = kv_len - kt;
+    const uint32_t n_records = rows_left >= kKvTile
+                                   ? (uint32_t)kKvTile * row_bytes
+                                   : (uint32_t)rows_left * row_bytes - (uint32_t)hk * L::kRowBytes;
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)n_records, kBufferFlags);
 #pragma unroll
@@ -265,16 +267,19 @@ struct TileScores {
 
 // Mask the scores of tile t: -inf where the key is past the stored keys or
 // (causal) after the query's position.  Only tiles on the diagonal or at the
-// end of the keys need it.
+// end of the keys need it.  A key is visible iff its offset within the lane's
+// key pattern is at most lim, the last visible key relative to the lane's
+// first key of the tile (so each score costs one compare and one select).
 template <bool CAUSAL>
 __device__ __forceinline__ void mask_scores(TileScores& s, int t, int q_pos, int kv_len, int g) {
+    const int last = CAUSAL ? min(q_pos, kv_len - 1) : kv_len - 1;
+    const int lim = last - (t * kKvTile + 4 * g);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int key = t * kKvTile + acc_key(kb, i, g);
-            const bool ok = key < kv_len && (!CAUSAL || key <= q_pos);
-            s.b[kb][i] = ok ? s.b[kb][i] : -INFINITY;
+            const int off = acc_key(kb, i, 0);
+            s.b[kb][i] = off <= lim ? s.b[kb][i] : -INFINITY;
         }
 }
 
@@ -306,7 +311,7 @@ __device__ __forceinline__ typename Operand<T>::x8 load_vt_slot(const char* vtil
 // With PREFETCH_V the last four slots also read phase B's first four V^T
 // fragments.  Hard scheduling barriers between slots keep every K read four
 // MFMAs ahead of its use and the exponentials spread under the MFMAs.
-template <int HD, typename T, bool HAS_CUR, bool HAS_NEXT, bool PREFETCH_V>
+template <int HD, typename T, bool HAS_CUR, bool HAS_NEXT, bool PREFETCH_V, bool PRIO>
 __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
                                         const typename Operand<T>::x8 (&qb)[HD / 16],
                                         const TileScores& sc, TileScores& sn,
@@ -349,6 +354,8 @@ __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
 #pragma unroll
         for (int i = 0; i < 4; ++i) kf[i] = kread(i);
     }
+    // Optional issue priority for the VALU-bound phase (the kernel's PRIO).
+    if (HAS_CUR && PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
         __builtin_amdgcn_sched_barrier(0);
@@ -371,6 +378,7 @@ __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
         asm volatile("" : "+v"(lsum));
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (HAS_CUR && PRIO) __builtin_amdgcn_s_setprio(0);
     if (HAS_NEXT) {
         sn.b[0] = acc[0];
         sn.b[1] = acc[1];
@@ -444,11 +452,21 @@ struct SplitWs {
     float* o;
 };
 
-template <int HD, typename TI, typename TO, bool CAUSAL>
+// pair_span > 0 (unsplit launches with a head count divisible by 8) reorders
+// the first dispatch wave so that heavy and light query tiles share CUs.
+// PRIO raises a wavefront's issue priority during phase A.  Two work-groups
+// share each SIMD, and they overlap best when the one in its VALU-bound
+// phase A issues first while the other's pure-MFMA phase B fills the gaps;
+// the planner picks the other instantiation where one heavy query tile sets
+// the kernel's length, since there the default arbitration (the older,
+// heavier work-group first) keeps that tile moving.  A compile-time choice:
+// a run-time branch around the priority changes measured several per cent
+// slower, as it splits the scheduled step.
+template <int HD, typename TI, typename TO, bool CAUSAL, bool PRIO>
 __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel(
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ v, TO* __restrict__ out,
     int q_len, int kv_len, int n_q_heads, int n_kv_heads, int n_q_tiles, float c2, int q_mode,
-    int n_splits, int* __restrict__ ws_ctr, float* __restrict__ ws_lw, float* __restrict__ ws_o) {
+    int n_splits, int pair_span, int* __restrict__ ws_ctr, float* __restrict__ ws_lw, float* __restrict__ ws_o) {
     using L = Tile<HD>;
     using Op = Operand<TI>;
     using X8 = typename Op::x8;
@@ -480,7 +498,15 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     int h, rank, split = 0;
     if ((n_q_heads % kXcds) == 0) {
         const int per_xcd = n_q_heads / kXcds;
-        const int local = b / kXcds;
+        int local = b / kXcds;
+        // Heavy-light pairing (pair_span = the CUs of one XCD, 0 = off): the
+        // dispatcher places an XCD's first-wave local indices k and
+        // k + pair_span on the same CU, so reversing the order of the second
+        // pair_span items pairs the heaviest query tiles with the lightest.
+        if (pair_span > 0) {
+            const int hi = min(2 * pair_span, n_q_tiles * per_xcd);
+            if (local >= pair_span && local < hi) local = pair_span + hi - 1 - local;
+        }
         rank = local / (per_xcd * n_splits);
         const int rem = local % (per_xcd * n_splits);
         split = rem / per_xcd;
@@ -518,12 +544,15 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
         n_tiles = (split == n_splits - 1 ? n_all : (split + 1) * shared / n_splits) - t_lo;
     }
     auto kv_row = [&](int i) { return (t_lo + i) * kKvTile; };
+    const uint32_t kv_row_bytes = (uint32_t)n_kv_heads * L::kRowBytes;
+    const char* const k_head = reinterpret_cast<const char*>(k) + (size_t)hk * L::kRowBytes;
+    const char* const v_head = reinterpret_cast<const char*>(v) + (size_t)hk * L::kRowBytes;
 
     // Staging schedule: K tile t is copied two tiles ahead of its use in
     // phase A, V tile t one tile ahead of its use in phase B.
-    stage_tile<HD>(k, n_kv_heads, hk, kv_len, kv_row(0), kbuf(0), wave, lane);
-    stage_tile<HD>(v, n_kv_heads, hk, kv_len, kv_row(0), vbuf(0), wave, lane);
-    if (n_tiles > 1) stage_tile<HD>(k, n_kv_heads, hk, kv_len, kv_row(1), kbuf(1), wave, lane);
+    stage_tile<HD>(k_head, kv_row_bytes, hk, kv_len, kv_row(0), kbuf(0), wave, lane);
+    stage_tile<HD>(v_head, kv_row_bytes, hk, kv_len, kv_row(0), vbuf(0), wave, lane);
+    if (n_tiles > 1) stage_tile<HD>(k_head, kv_row_bytes, hk, kv_len, kv_row(1), kbuf(1), wave, lane);
 
     // Q^T as the B operand: lane (l32, g) holds q[my_q][h][16t + 8g .. +8).
     // q_mode 1 negates Q (negative scale: a sign-bit flip, exact), 2 zeroes
@@ -558,7 +587,7 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     __syncthreads();
     {
         X8 vf_unused[4];
-        phase_a<HD, TI, false, true, false>(kbuf(0), qb, sa, sa, pb, l_part, m_ref, c2, l32, g, nullptr,
+        phase_a<HD, TI, false, true, false, PRIO>(kbuf(0), qb, sa, sa, pb, l_part, m_ref, c2, l32, g, nullptr,
                                             vt_off, vf_unused);
         if (tile_needs_mask<CAUSAL>(t_lo, pos_w, kv_len)) mask_scores<CAUSAL>(sa, t_lo, q_pos, kv_len, g);
         float mx = fmaxf(sa.b[0][0], sa.b[1][0]);
@@ -574,10 +603,10 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     auto step = [&](int j, TileScores& sc, TileScores& sn) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (j + 2 < n_tiles) stage_tile<HD>(k, n_kv_heads, hk, kv_len, kv_row(j + 2), kbuf(j + 2), wave, lane);
-        stage_tile<HD>(v, n_kv_heads, hk, kv_len, kv_row(j + 1), vbuf(j + 1), wave, lane);
+        if (j + 2 < n_tiles) stage_tile<HD>(k_head, kv_row_bytes, hk, kv_len, kv_row(j + 2), kbuf(j + 2), wave, lane);
+        stage_tile<HD>(v_head, kv_row_bytes, hk, kv_len, kv_row(j + 1), vbuf(j + 1), wave, lane);
         X8 vf[4];
-        phase_a<HD, TI, true, true, true>(kbuf(j + 1), qb, sc, sn, pb, l_part, m_ref, c2, l32, g, vbuf(j),
+        phase_a<HD, TI, true, true, true, PRIO>(kbuf(j + 1), qb, sc, sn, pb, l_part, m_ref, c2, l32, g, vbuf(j),
                                           vt_off, vf);
         if (tile_needs_mask<CAUSAL>(t_lo + j + 1, pos_w, kv_len))
             mask_scores<CAUSAL>(sn, t_lo + j + 1, q_pos, kv_len, g);
@@ -589,7 +618,7 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         X8 vf[4];
-        phase_a<HD, TI, true, false, true>(nullptr, qb, sc, sc, pb, l_part, m_ref, c2, l32, g, vbuf(j),
+        phase_a<HD, TI, true, false, true, PRIO>(nullptr, qb, sc, sc, pb, l_part, m_ref, c2, l32, g, vbuf(j),
                                            vt_off, vf);
         phase_b<HD, TI, false>(vbuf(j), pb, oacc, sc, c2, l32, g, vt_off, vf);
     };
@@ -724,21 +753,23 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     }
 }
 
-// Entry of the (HD, input type, output type, causal) instantiation.
+// Entry of the (HD, input type, output type, causal, phase priority)
+// instantiation.
+template <int HD, typename TI, typename TO>
+const void* pick_kernel_t(bool causal, bool prio) {
+    if (causal)
+        return prio ? reinterpret_cast<const void*>(&fa_prefill_kernel<HD, TI, TO, true, true>)
+                    : reinterpret_cast<const void*>(&fa_prefill_kernel<HD, TI, TO, true, false>);
+    return prio ? reinterpret_cast<const void*>(&fa_prefill_kernel<HD, TI, TO, false, true>)
+                : reinterpret_cast<const void*>(&fa_prefill_kernel<HD, TI, TO, false, false>);
+}
+
 template <int HD>
-const void* pick_kernel(bool in_bf16, bool out_f32, bool causal) {
-    if (in_bf16) {
-        if (out_f32)
-            return causal ? reinterpret_cast<const void*>(&fa_prefill_kernel<HD, __bf16, float, true>)
-                          : reinterpret_cast<const void*>(&fa_prefill_kernel<HD, __bf16, float, false>);
-        return causal ? reinterpret_cast<const void*>(&fa_prefill_kernel<HD, __bf16, __bf16, true>)
-                      : reinterpret_cast<const void*>(&fa_prefill_kernel<HD, __bf16, __bf16, false>);
-    }
-    if (out_f32)
-        return causal ? reinterpret_cast<const void*>(&fa_prefill_kernel<HD, _Float16, float, true>)
-                      : reinterpret_cast<const void*>(&fa_prefill_kernel<HD, _Float16, float, false>);
-    return causal ? reinterpret_cast<const void*>(&fa_prefill_kernel<HD, _Float16, _Float16, true>)
-                  : reinterpret_cast<const void*>(&fa_prefill_kernel<HD, _Float16, _Float16, false>);
+const void* pick_kernel(bool in_bf16, bool out_f32, bool causal, bool prio) {
+    if (in_bf16)
+        return out_f32 ? pick_kernel_t<HD, __bf16, float>(causal, prio) : pick_kernel_t<HD, __bf16, __bf16>(causal, prio);
+    return out_f32 ? pick_kernel_t<HD, _Float16, float>(causal, prio)
+                   : pick_kernel_t<HD, _Float16, _Float16>(causal, prio);
 }
 
 }  // namespace

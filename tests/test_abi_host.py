@@ -123,6 +123,33 @@ def test_plan_geometry(S, nq, nkv, causal, hd):
     assert p.kv_tiles_visited == tiles * nq
 
 
+@pytest.mark.parametrize("nq,nkv,q_len,kv_len,hd,causal,expect", [
+    (32, 32, 2048, 2048, 128, 1, 0),    # heaviest tile 32 key tiles vs 17 per slot
+    (32, 32, 2659, 2659, 128, 1, 0),    # 42 vs 28.9
+    (32, 8, 4096, 4096, 128, 1, 1),     # 64 vs 66
+    (32, 8, 16384, 16384, 128, 1, 1),   # 256 vs 1032
+    (32, 32, 2659, 2659, 128, 0, 1),    # non-causal: every work-group equal
+    (64, 64, 2659, 2659, 64, 1, 1),     # 1344 work-groups: 42 vs 57.75
+    (16, 16, 2659, 2659, 256, 1, 0),    # one work-group per CU: 42 vs 28.9
+    (32, 32, 512, 4096, 128, 1, 1),     # split chunk: parts of equal length
+    (2, 2, 256, 256, 128, 1, 0),        # 4 work-groups of 4, 4, 2, 2 tiles
+])
+def test_plan_phase_priority(nq, nkv, q_len, kv_len, hd, causal, expect):
+    """Phase-A issue priority is planned for throughput-bound launches only:
+    heaviest work-group <= 1.25 x the average key tiles per occupied slot
+    (the default 256-CU device, 2 work-groups per CU, 1 for head_dim 256)."""
+    p = fa.fa_prefill_chunk_plan(nq, nkv, q_len, kv_len, hd, causal)
+    assert p.phase_priority == expect
+    tiles, max_tiles = 0, 0
+    for t in range(p.n_q_tiles):
+        last = kv_len - q_len + (t + 1) * p.q_tile
+        n = math.ceil((min(kv_len, last) if causal else kv_len) / p.kv_tile)
+        tiles, max_tiles = tiles + n, max(max_tiles, n)
+    occupied = min(p.n_groups, p.groups_per_cu * 256)
+    heaviest = math.ceil(max_tiles / p.kv_splits)
+    assert p.phase_priority == int(heaviest * occupied <= 1.25 * tiles * nq)
+
+
 def test_plan_lds_limit_fails_loudly():
     p = fa.fa_prefill_plan(32, 32, 2659, 128, 1)
     fa.fa_prefill_plan(32, 32, 2659, 128, 1, max_lds_bytes=p.lds_bytes)  # exactly fits
