@@ -641,15 +641,34 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     TO* const orow = out + ((size_t)my_q * n_q_heads + h) * HD + 4 * g;
     if (n_splits == 1) {
-        if (my_q < q_len) {
+        // Row-major output through LDS.  The accumulators hold one query per
+        // lane, so storing them directly writes 32 rows x 32 bytes per
+        // instruction.  Instead each wave writes its 32 rows into LDS (the
+        // 16-byte chunk c of row r at chunk c ^ (r & 15), conflict-free for
+        // both patterns) and reads them back as whole rows, two 512-byte rows
+        // per store instruction (head_dim 128).  After the barrier every wave
+        // has finished its last P.V, so the K/V stages are free.
+        __syncthreads();
+        constexpr int kRowChunks = HD / 4;  // 16-byte chunks of an f32 row
+        float* const ot = reinterpret_cast<float*>(lds) + wave * kQRowsPerWave * HD;
+        auto chunk_at = [&](int r, int c) { return ot + r * HD + ((c ^ (r & 15)) << 2); };
 #pragma unroll
-            for (int db = 0; db < ND; ++db)
+        for (int db = 0; db < ND; ++db)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const floatx4 o = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv,
-                                       oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv};
-                    store4(orow + 32 * db + 8 * jj, o);
-                }
+            for (int jj = 0; jj < 4; ++jj) {
+                const floatx4 o = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv,
+                                   oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv};
+                *reinterpret_cast<floatx4*>(chunk_at(l32, 8 * db + 2 * jj + g)) = o;
+            }
+        // The wave reads back what its own lanes wrote.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        constexpr int kRowsPerRead = kWaveSize / kRowChunks;
+        const int rr = lane / kRowChunks, c = lane % kRowChunks;
+#pragma unroll
+        for (int kk = 0; kk < kQRowsPerWave / kRowsPerRead; ++kk) {
+            const int r = kk * kRowsPerRead + rr;
+            const floatx4 o = *reinterpret_cast<const floatx4*>(chunk_at(r, c));
+            if (qw + r < q_len) store4(out + ((size_t)(qw + r) * n_q_heads + h) * HD + 4 * c, o);
         }
         return;
     }
