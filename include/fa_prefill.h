@@ -48,8 +48,9 @@
  * overlap q, k or v.
  *
  * Workspace.  A launch whose grid would leave work-group slots idle (a short
- * chunk over a long KV cache: fa_plan.kv_splits > 1) splits each query tile's
- * key range over several work-groups and needs device scratch of
+ * chunk over a long KV cache, or a prefill of few heads: fa_plan.kv_splits > 1)
+ * splits the key range of each query tile that is long enough over several
+ * work-groups and needs device scratch of
  * fa_plan.workspace_bytes for their partial results.  The library owns it:
  * one block per (device, stream), allocated and zeroed by the first call on
  * that pair that needs it, grown by a later call that needs more (after
@@ -108,8 +109,11 @@ typedef struct fa_plan {
     int kv_tile;             /* key/value rows per LDS tile                       */
     int waves_per_group;     /* 64-lane wavefronts per work-group                 */
     int threads_per_group;   /* waves_per_group * 64                              */
-    int kv_splits;           /* work-groups sharing one query tile's key range
-                                (split-KV; 1 = no split)                          */
+    int kv_splits;           /* most work-groups sharing one query tile's key range
+                                (split-KV; 1 = no split).  A tile takes as many as
+                                keep each part >= 20 of the key tiles in front of
+                                its first query, at least one; the grid launches
+                                kv_splits per tile and the surplus ones exit    */
     int n_q_tiles;           /* ceil(q_len / q_tile)                              */
     long long n_groups;      /* work-groups launched: n_q_tiles * n_q_heads * kv_splits,
                                 the item count n_q_tiles * n_q_heads rounded up to a

@@ -56,26 +56,63 @@ int check_dtypes(int in_dtype, int out_dtype) {
     return FA_OK;
 }
 
-// Split-KV count for a launch of `items` query tiles.  Splitting pays only
-// when the grid leaves resident work-group slots idle (a whole-sequence
-// prefill that fills the slots measured slower when split: every extra
-// work-group adds its start-up latency).  Each part must begin at or before
-// the first query position of its tile, so that every query row sees a key
-// in every part (the parts share out the tiles that start at or before that
-// position; the last part also takes the diagonal and tail tiles): with the
-// causal mask this needs a KV cache in front of the chunk.  All parts of a
-// tile run on one XCD (they meet through its L2); the kernel's work-group
-// mapping guarantees it for every head count.
-static int choose_splits(long long items, long long q_off, long long kv_len, bool causal, int n_cus,
-                         int head_dim) {
+// Split-KV count for a launch of n_q_tiles x n_heads query tiles.  Splitting
+// pays only when the grid leaves resident work-group slots idle (a
+// whole-sequence prefill that fills the slots measured slower when split:
+// every extra work-group adds its start-up latency).  Each part must begin at
+// or before the first query position of its tile, so that every query row
+// sees a key in every part (the parts share out the tiles that start at or
+// before that position; the last part also takes the diagonal and tail
+// tiles), and each part covers at least kMinSplitTiles of those shared tiles.
+// A launch of n parts gives every tile as many of them as its own shared
+// range allows, so the early tiles of a causal prefill, which have few keys
+// in front of them, stay whole.  Among the admissible n the planner takes the
+// one with the shortest longest part, counting a part kSharedPartCost times
+// longer once the working work-groups outnumber the CUs (a second
+// work-group on a CU adds little throughput, and the younger of the two is
+// starved), and the smallest n on a tie.  All parts of a tile run on one XCD
+// (they meet through its L2); the kernel's work-group mapping guarantees it
+// for every head count.
+static long long part_count(long long n, long long shared) {
+    const long long p = shared / kMinSplitTiles;
+    return p < 1 ? 1 : (p < n ? p : n);
+}
+
+static int choose_splits(long long n_q_tiles, long long n_heads, long long q_off, long long kv_len, bool causal,
+                         int n_cus, int head_dim) {
+    const long long items = n_q_tiles * n_heads;
     const long long slots = (long long)groups_per_cu(head_dim) * n_cus;
     if (items <= 0 || items * 2 > slots) return 1;
-    // tiles shared out, for the tile with the fewest (the first query tile)
-    const long long shared = causal ? q_off / kKvTile + 1 : (kv_len + kKvTile - 1) / kKvTile;
-    long long n = slots / items;
-    n = n < kMaxSplits ? n : kMaxSplits;
-    n = n < shared / kMinSplitTiles ? n : shared / kMinSplitTiles;
-    return n >= 2 ? (int)n : 1;
+    auto shared_of = [&](long long t, long long n_all) {
+        return causal ? (q_off + t * kQTile) / kKvTile + 1 : n_all;
+    };
+    auto n_all_of = [&](long long t) {
+        const long long end = causal ? (q_off + (t + 1) * kQTile < kv_len ? q_off + (t + 1) * kQTile : kv_len) : kv_len;
+        return (end + kKvTile - 1) / kKvTile;
+    };
+    long long n_max = slots / items;
+    n_max = n_max < kMaxSplits ? n_max : kMaxSplits;
+    const long long last = n_all_of(n_q_tiles - 1);
+    n_max = n_max < shared_of(n_q_tiles - 1, last) / kMinSplitTiles ? n_max : shared_of(n_q_tiles - 1, last) / kMinSplitTiles;
+    int best = 1;
+    double best_cost = 0.0;
+    for (long long n = 1; n <= (n_max > 1 ? n_max : 1); ++n) {
+        long long working = 0, longest = 0;
+        for (long long t = 0; t < n_q_tiles; ++t) {
+            const long long n_all = n_all_of(t), shared = shared_of(t, n_all);
+            const long long parts = n == 1 ? 1 : part_count(n, shared);
+            working += parts;
+            const long long tail = n_all - (parts - 1) * shared / parts;  // the last part is the longest
+            longest = tail > longest ? tail : longest;
+        }
+        working *= n_heads;
+        const double cost = (double)longest * (working > n_cus ? kSharedPartCost : 1.0);
+        if (n == 1 || cost < best_cost) {
+            best = (int)n;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 // Phase-A issue priority (the kernel's prio_a): on when the launch is
@@ -122,7 +159,8 @@ int make_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim
                     lds_bytes(head_dim), max_lds_bytes);
     if (n_cus <= 0) n_cus = 256;
     const long long items = n_q_tiles * (long long)n_q_heads;
-    const int splits = choose_splits(items, (long long)kv_len - q_len, kv_len, causal != 0, n_cus, head_dim);
+    const int splits =
+        choose_splits(n_q_tiles, n_q_heads, (long long)kv_len - q_len, kv_len, causal != 0, n_cus, head_dim);
     // A split launch whose head count is not a multiple of 8 pads the items
     // to a multiple of 8 (see the kernel's work-group mapping).
     const long long grid_items =

@@ -536,12 +536,18 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     // Key tiles [t_lo, t_lo + n_tiles) of this work-group.  A split tile's
     // parts share out the tiles that start at or before the tile's first
     // query position (so every query row sees a key in every part); the last
-    // part also takes the diagonal and tail tiles.
-    int t_lo = 0, n_tiles = n_all;
+    // part also takes the diagonal and tail tiles.  n_splits is the launch's
+    // part count; a query tile takes as many of them (at least one) as keep
+    // each part at least kMinSplitTiles of those shared tiles long, so the
+    // early tiles of a causal prefill stay whole, and the surplus
+    // work-groups of a tile exit at once.
+    int t_lo = 0, n_tiles = n_all, parts = 1;
     if (n_splits > 1) {
         const int shared = CAUSAL ? (q_off + q0) / kKvTile + 1 : n_all;
-        t_lo = split * shared / n_splits;
-        n_tiles = (split == n_splits - 1 ? n_all : (split + 1) * shared / n_splits) - t_lo;
+        parts = min(n_splits, max(1, shared / kMinSplitTiles));
+        if (split >= parts) return;  // uniform per work-group
+        t_lo = split * shared / parts;
+        n_tiles = (split == parts - 1 ? n_all : (split + 1) * shared / parts) - t_lo;
     }
     auto kv_row = [&](int i) { return (t_lo + i) * kKvTile; };
     const uint32_t kv_row_bytes = (uint32_t)n_kv_heads * L::kRowBytes;
@@ -640,7 +646,7 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     const float l_tot = pair_sum(l_part);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     TO* const orow = out + ((size_t)my_q * n_q_heads + h) * HD + 4 * g;
-    if (n_splits == 1) {
+    if (parts == 1) {
         // Row-major output through LDS.  The accumulators hold one query per
         // lane, so storing them directly writes 32 rows x 32 bytes per
         // instruction.  Instead each wave writes its 32 rows into LDS (the
@@ -707,7 +713,7 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     if (tid == 0)
         *merge_flag = __hip_atomic_fetch_add(ws_ctr + item, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (*merge_flag != n_splits - 1) return;
+    if (*merge_flag != parts - 1) return;
     asm volatile("buffer_inv sc0" ::: "memory");
     if (tid == 0) __hip_atomic_store(ws_ctr + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (my_q < q_len) {
@@ -715,13 +721,13 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
         float mx = -INFINITY;
 #pragma unroll
         for (int p = 0; p < kMaxSplits; ++p) {
-            wt[p] = p < n_splits ? ws_lw[(part0 + p) * kQTile + row] : -INFINITY;
+            wt[p] = p < parts ? ws_lw[(part0 + p) * kQTile + row] : -INFINITY;
             mx = fmaxf(mx, wt[p]);
         }
         float wsum = 0.0f;
 #pragma unroll
         for (int p = 0; p < kMaxSplits; ++p) {
-            wt[p] = p < n_splits ? __builtin_amdgcn_exp2f(wt[p] - mx) : 0.0f;
+            wt[p] = p < parts ? __builtin_amdgcn_exp2f(wt[p] - mx) : 0.0f;
             wsum += wt[p];
         }
         const float norm = 1.0f / wsum;
@@ -737,12 +743,12 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
                 for (int jj = 0; jj < 4; ++jj) acc[d][jj] = floatx4{};
 #pragma unroll
             for (int p0 = 0; p0 < kMaxSplits; p0 += 4) {
-                if (p0 >= n_splits) break;
+                if (p0 >= parts) break;
                 floatx4 x[4][2][4];
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) {
                     const int p = p0 + pp;
-                    if (p < n_splits) {
+                    if (p < parts) {
                         const float* po = ws_o + ((part0 + p) * kQTile + row) * HD + 4 * g;
 #pragma unroll
                         for (int d = 0; d < 2; ++d)
@@ -754,7 +760,7 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) {
                     const int p = p0 + pp;
-                    if (p >= n_splits) break;
+                    if (p >= parts) break;
 #pragma unroll
                     for (int d = 0; d < 2; ++d)
 #pragma unroll

@@ -113,6 +113,10 @@ WORKLOADS = {
         "long_16k", "long GQA causal prefill, 32 q / 8 kv heads, S=16384, hd=128", 32, 8, 16384, seed=5,
         oracle_rows=256,
     ),
+    "one_head_16k": Workload(
+        "one_head_16k", "causal prefill of one head, S=16384, hd=128 (128 query tiles under-fill the device: "
+        "the long tiles' key ranges are split)", 1, 1, 16384, seed=11, oracle_rows=256,
+    ),
     "chunk_512_4k": Workload(
         "chunk_512_4k", "7B-layer chunked causal prefill: 512 new tokens over a 3584-token KV cache, "
         "32/32 heads, hd=128", 32, 32, 4096, seed=6, q_rows=512,

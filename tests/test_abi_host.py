@@ -111,8 +111,9 @@ def test_plan_geometry(S, nq, nkv, causal, hd):
     assert p.threads_per_group == 64 * p.waves_per_group
     assert p.q_tile == 32 * p.waves_per_group
     assert p.n_q_tiles == math.ceil(S / p.q_tile)
-    # a whole-sequence prefill is never split (its first query tile has no
-    # keys in front of it) and needs no workspace
+    # these whole-sequence prefills fill the device, or their query tiles are
+    # too short to split into parts of >= 20 shared key tiles: no split, no
+    # workspace
     assert p.kv_splits == 1 and p.workspace_bytes == 0
     assert p.n_groups == p.n_q_tiles * nq
     # KV tiles visited: causal groups stop at their last query row
@@ -227,6 +228,29 @@ def workspace_bytes(items, parts, q_tile=128):
 ])
 def test_chunk_plan_splits(nq, q_len, kv_len, causal, splits):
     p = fa.fa_prefill_chunk_plan(nq, nq // 2 if nq % 2 == 0 else nq, q_len, kv_len, 128, causal)
+    assert p.kv_splits == splits
+    items = p.n_q_tiles * nq
+    grid_items = items if splits == 1 or nq % 8 == 0 else -(-items // 8) * 8
+    assert p.n_groups == grid_items * splits
+    assert p.workspace_bytes == (workspace_bytes(items, items * splits) if splits > 1 else 0)
+
+
+@pytest.mark.parametrize("S,nq,nkv,splits", [
+    (16384, 1, 1, 4),   # 128 query tiles on 512 slots: the last tile's 256 keys in 4 parts
+    (8192, 2, 2, 4),    # 128 items; 4 parts cut the longest part to 33 tiles (tile 19's 40 then bind)
+    (8192, 3, 1, 2),    # 192 items: at most 2 parts per tile fit the slots
+    (4096, 4, 2, 2),    # 3 parts would leave tile 19's 40 unsplittable tiles the longest: the smaller count
+    (2659, 8, 8, 2),    # 168 items
+    (2659, 3, 3, 2),    # a head count that is not a multiple of 8 (items padded to 8)
+    (2048, 8, 8, 1),    # the last tile shares only 31 key tiles: parts would be shorter than 20
+    (2659, 32, 32, 1),  # 672 items fill the device
+])
+def test_plan_splits_few_head_prefill(S, nq, nkv, splits):
+    """A whole prefill of few heads under-fills the device: the planner splits
+    the long causal query tiles (those with >= 40 shared key tiles), picking
+    the part count whose longest part is shortest (a part costs 1.25x once the
+    working work-groups outnumber the 256 CUs), the smaller count on a tie."""
+    p = fa.fa_prefill_plan(nq, nkv, S, 128, 1)
     assert p.kv_splits == splits
     items = p.n_q_tiles * nq
     grid_items = items if splits == 1 or nq % 8 == 0 else -(-items // 8) * 8

@@ -75,6 +75,21 @@ def test_long_16k_sampled_rows(fa):
     assert within_tolerance(err), err
 
 
+def test_one_head_16k_sampled_rows(fa):
+    # the benchmark's few-head workload at its full size: its long query
+    # tiles run split over several work-groups
+    wl = WORKLOADS["one_head_16k"]
+    assert fa.fa_prefill_plan(1, 1, wl.seq_len, 128, 1).kv_splits > 1
+    q, k, v = make_inputs(wl)
+    got = _run(fa, q, k, v)
+    assert np.all(np.isfinite(got))
+    rows = row_subset(wl.seq_len, wl.oracle_rows, seed=wl.seed)
+    ref = attention_rows_blocked(q, k, v, SCALE, True, rows=rows, block=64)
+    err = parity_errors(got[rows], ref)
+    _report("one_head_16k (256 rows)", err)
+    assert within_tolerance(err), err
+
+
 TAIL_LENGTHS = [1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 95, 127, 128, 129, 191, 255, 257, 300]
 
 
@@ -324,6 +339,24 @@ def test_split_kv_any_head_count(fa, q_len, kv_len, heads):
     assert within_tolerance(err), err
     again = _run_chunk(fa, q, k, v)
     assert np.array_equal(got, again), "merge depends on arrival order"
+
+
+@pytest.mark.parametrize("S,heads", [
+    (8192, (1, 1)), (6000, (2, 1)), (4096, (4, 2)), (2659, (3, 3)), (2659, (8, 8)),
+])
+def test_split_whole_prefill_few_heads(fa, S, heads):
+    """A whole prefill of few heads splits its long causal query tiles (the
+    early tiles stay whole); every element against the oracle, and reruns
+    bitwise identical (the merge runs in part order)."""
+    nq, nkv = heads
+    plan = fa.fa_prefill_plan(nq, nkv, S, 128, 1)
+    assert plan.kv_splits > 1, "shape chosen to split"
+    q, k, v = make_custom_inputs(S, nq, nkv, seed=S + 11 * nq)
+    got = _run(fa, q, k, v)
+    err = parity_errors(got, attention_f64(q, k, v, SCALE, True))
+    _report(f"split prefill S={S} heads={heads} parts={plan.kv_splits}", err)
+    assert within_tolerance(err), err
+    assert np.array_equal(got, _run(fa, q, k, v)), "merge depends on arrival order"
 
 
 def test_split_kv_deterministic_and_peaked(fa):
