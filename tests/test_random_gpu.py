@@ -70,3 +70,46 @@ def test_random_case(fa, case):
     print(f"[random] {tag}: splits {plan.kv_splits} max_abs={err['max_abs']:.3e} max_rel={err['max_rel']:.3e}",
           flush=True)
     assert within_tolerance(err, atol, rtol), (tag, err)
+
+
+N_SPLIT_CASES = 12
+
+
+def _split_prefill_cases():
+    """Long prefills of few heads, whole or with a short cache in front: the
+    grid under-fills the device, so the long query tiles split (11 of the 12
+    cases; the twelfth, head_dim 256 with 144 query tiles, fills its 256
+    slots halfway and runs whole)."""
+    rng = np.random.Generator(np.random.PCG64(2027))
+    out = []
+    for i in range(N_SPLIT_CASES):
+        hd = int(rng.choice([64, 128, 256]))
+        in_dt = str(rng.choice(["f16", "bf16"]))
+        out_dt = str(rng.choice(["f32", in_dt]))
+        n_kv = int(rng.choice([1, 2]))
+        group = int(rng.choice([1, 2]))
+        kv_len = int(rng.integers(2600, 7000))
+        q_len = kv_len if rng.random() < 0.6 else int(rng.integers(kv_len // 2, kv_len + 1))
+        scale = float(np.float32(rng.choice([1.0, 0.5, -1.0]) / math.sqrt(hd)))
+        out.append((i, hd, in_dt, out_dt, n_kv * group, n_kv, q_len, kv_len, scale))
+    return out
+
+
+@pytest.mark.parametrize("case", _split_prefill_cases(), ids=lambda c: f"split{c[0]}")
+def test_random_split_prefill(fa, case):
+    i, hd, in_dt, out_dt, nq, nkv, q_len, kv_len, scale = case
+    tag = f"split{i}: hd{hd} {in_dt}->{out_dt} heads {nq}/{nkv} q_len {q_len} kv_len {kv_len} scale={scale:.4g}"
+    print(f"[random] {tag}", flush=True)
+    plan = fa.fa_prefill_chunk_plan(nq, nkv, q_len, kv_len, hd, 1)
+    q, k, v = make_custom_inputs(kv_len, nq, nkv, seed=3000 + i, head_dim=hd, q_len=q_len, in_dtype=in_dt)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    out = fa.attention(dq, dk, dv, scale, True, out_dtype=TORCH_DTYPES[out_dt])
+    again = fa.attention(dq, dk, dv, scale, True, out_dtype=TORCH_DTYPES[out_dt])
+    torch.cuda.synchronize()
+    assert torch.equal(out, again), tag + ": the merge depends on arrival order"
+    ref = attention_chunk_f64(q, k, v, scale, True)
+    atol, rtol = bar(in_dt)
+    err = parity_errors(out.float().cpu().numpy().astype(np.float64), ref, OUT_UNIT[out_dt])
+    print(f"[random] {tag}: splits {plan.kv_splits} max_abs={err['max_abs']:.3e} max_rel={err['max_rel']:.3e}",
+          flush=True)
+    assert within_tolerance(err, atol, rtol), (tag, err)
