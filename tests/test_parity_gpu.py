@@ -299,9 +299,9 @@ def test_chunk_error_paths_on_device(fa):
 
 
 # ---------------------------------------------------------------- split-KV
-# Grids that would leave slots idle (a short chunk over a long cache) split each
-# query tile's key range over several work-groups and merge their partial
-# softmax states.  Head counts here are multiples of 8, so the split path runs.
+# Grids that would leave slots idle (a short chunk over a long cache, or a long
+# prefill of few heads) split the key range of each long query tile over
+# several work-groups and merge their partial softmax states.
 
 def _chunk_plan(fa, nq, nkv, q_len, kv_len, causal=True):
     return fa.fa_prefill_chunk_plan(nq, nkv, q_len, kv_len, 128, int(causal))
