@@ -6,7 +6,13 @@
 One step = one fa_prefill launch over the whole workload (32 heads x 2659
 tokens x head_dim 128, causal, f16 in, f32 out by default), inputs resident in
 HBM.  W untimed steps, then K steps back to back on one stream, bracketed by
-HIP events and device synchronisation.  Prints one JSON line.
+device synchronisation and split into B bursts (default 7 x 50) with a HIP
+event on the launch stream at every burst boundary.  The time per step is the
+median burst's time per launch (p10 / p90 / mean over bursts are reported
+too, so the clock's sag under sustained load shows), warm L2 / MALL.  A cold
+figure follows: launches each preceded by a 1 GiB scrub that evicts the
+inputs from the caches, each timed on its own.  Prints one JSON line
+(``--workload all``: one line per configuration).
 
 A K/V producer workload (--workload kv_store_2659 etc.) times fa_store_kv
 instead: one step = one launch storing the workload's K and V, rotating over
@@ -205,12 +211,97 @@ def store_bench(args, key) -> int:
     return 0
 
 
+def burst_split(steps: int, bursts: int) -> list:
+    """Sizes of `bursts` near-equal bursts covering exactly `steps` launches."""
+    b = max(1, min(bursts, steps))
+    return [steps // b + (1 if i < steps % b else 0) for i in range(b)]
+
+
+def percentile(xs, p: float) -> float:
+    """Linear-interpolated percentile p (0..100) of a non-empty list."""
+    s = sorted(xs)
+    if len(s) == 1:
+        return s[0]
+    pos = (len(s) - 1) * p / 100.0
+    lo = int(pos)
+    hi = min(lo + 1, len(s) - 1)
+    return s[lo] + (s[hi] - s[lo]) * (pos - lo)
+
+
+def time_bursts(launch, stream, steps: int, warmup: int, bursts: int) -> dict:
+    """Warm up, then time `steps` launches in bursts on `stream`.
+
+    Every burst boundary carries a HIP event recorded on the launch stream,
+    so the per-burst times are device times of back-to-back launches; the
+    whole region is bracketed by device synchronisation.  Returns the
+    per-launch milliseconds of each burst, their median / p10 / p90, the
+    mean over all launches and the launch statuses.
+    """
+    import torch
+
+    sizes = burst_split(steps, bursts)
+    statuses = []
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            statuses.append(launch())
+        stream.synchronize()
+        events = [torch.cuda.Event(enable_timing=True) for _ in range(len(sizes) + 1)]
+        torch.cuda.synchronize()
+        events[0].record(stream)
+        for i, n in enumerate(sizes):
+            for _ in range(n):
+                statuses.append(launch())
+            events[i + 1].record(stream)
+        events[-1].synchronize()
+        torch.cuda.synchronize()
+    per_launch = [events[i].elapsed_time(events[i + 1]) / n for i, n in enumerate(sizes)]
+    total = events[0].elapsed_time(events[-1])
+    return {
+        "burst_ms_per_launch": per_launch,
+        "burst_sizes": sizes,
+        "median": percentile(per_launch, 50.0),
+        "p10": percentile(per_launch, 10.0),
+        "p90": percentile(per_launch, 90.0),
+        "mean": total / steps,
+        "region_ms": total,
+        "statuses": statuses,
+    }
+
+
+def time_cold(launch, stream, n: int, scrub_bytes: int = 1 << 30) -> list:
+    """Per-launch milliseconds of n launches, each after a scrub of scrub_bytes.
+
+    The scrub writes a buffer four times the size of the MI355X's 256 MB
+    Infinity Cache, which evicts the inputs from the L2s and the MALL; only
+    the launch itself lies between its two events.
+    """
+    import torch
+
+    scrub = torch.empty(scrub_bytes // 4, dtype=torch.float32, device=stream.device)
+    times = []
+    with torch.cuda.stream(stream):
+        for _ in range(n):
+            scrub.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch()
+            b.record(stream)
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+    del scrub
+    return times
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=None, help="workload key (default: the headline one)")
+    ap.add_argument("--steps", type=int, default=350, help="timed launches (split into --bursts)")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--bursts", type=int, default=7, help="bursts the timed launches are split into")
+    ap.add_argument("--cold", type=int, default=10, metavar="N",
+                    help="cold-cache launches after the warm bursts (0: skip)")
+    ap.add_argument("--workload", default=None,
+                    help="workload key (default: the headline one; 'all': one line per configuration)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of attention, run --steps device-to-device copies of MIB MiB "
@@ -222,14 +313,13 @@ def main() -> int:
               "(attention shards over heads with no exchange, but no multi-GPU path is built)",
               file=sys.stderr)
         return 2
-    if args.steps < 1 or args.warmup < 0:
-        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+    if args.steps < 1 or args.warmup < 0 or args.bursts < 1 or args.cold < 0:
+        print("bench.py: --steps and --bursts must be >= 1, --warmup and --cold >= 0", file=sys.stderr)
         return 2
 
     import torch
 
-    import prefill_attention_amd as fa
-    from prefill_attention_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+    from prefill_attention_amd.workloads import HEADLINE, WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -249,18 +339,35 @@ def main() -> int:
     key = args.workload or HEADLINE
     if key in STORE_WORKLOADS:
         return store_bench(args, key)
+    if key == "all":
+        rc = 0
+        for k in CONFIG_KEYS:
+            rc = rc or attention_bench(args, k)
+        return rc
     if key not in WORKLOADS:
         print(f"bench.py: unknown workload {key!r}; known: {sorted(WORKLOADS) + sorted(STORE_WORKLOADS)}",
               file=sys.stderr)
         return 2
+    return attention_bench(args, key)
+
+
+# The five configurations the throughput is reported on (``--workload all``).
+CONFIG_KEYS = ("tiny", "7b_2k", "7b_2659", "gqa_4k", "long_16k")
+
+
+def attention_bench(args, key) -> int:
+    """Time one attention workload; print its JSON line."""
+    import torch
+
+    import prefill_attention_amd as fa
+    from prefill_attention_amd.binding import FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32
+    from prefill_attention_amd.workloads import HEADLINE, TORCH_DTYPES, WORKLOADS, make_inputs
+
     wl = WORKLOADS[key]
     fa.load_library()
     dev = torch.device("cuda:0")
     q, k, v = make_inputs(wl)
     dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
-    from prefill_attention_amd.binding import FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32
-    from prefill_attention_amd.workloads import TORCH_DTYPES
-
     scale = wl.scale
     out_dt = TORCH_DTYPES[wl.out_dtype]
     out = torch.empty((wl.q_len, wl.n_q_heads, wl.head_dim), dtype=out_dt, device=dev)
@@ -289,23 +396,16 @@ def main() -> int:
                      wl.n_kv_heads, wl.seq_len, wl.head_dim, scale, int(wl.causal), stream.cuda_stream)
     fa.attention(dq, dk, dv, scale, wl.causal, out=out, stream=stream)  # checked call first
     torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            entry(*call_args)
-        stream.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        statuses = [entry(*call_args) for _ in range(args.steps)]
-        end.record(stream)
-        end.synchronize()
-        torch.cuda.synchronize()
+    launch = lambda: entry(*call_args)  # noqa: E731
+    t = time_bursts(launch, stream, args.steps, args.warmup, args.bursts)
+    cold = time_cold(launch, stream, args.cold) if args.cold > 0 else []
+    statuses = t["statuses"]
     if any(statuses):
         print(f"bench.py: the entry point returned {set(statuses)}", file=sys.stderr)
         return 1
-    region_ms = start.elapsed_time(end)
-    ms_per_step = region_ms / args.steps
+    ms_per_step = t["median"]
     tflops = wl.flop / (ms_per_step * 1e-3) / 1e12
+    tf = lambda ms: round(wl.flop / (ms * 1e-3) / 1e12, 2)  # noqa: E731
 
     traffic = measured_traffic(key)
     min_bytes = (q.numel() + k.numel() + v.numel()) * 2 + out.numel() * out.element_size()
@@ -326,6 +426,20 @@ def main() -> int:
         "config": {**wl.describe(), "workload_key": key, "plan": plan.as_dict()},
         "pct_peak": round(100.0 * tflops / PEAK_F16_TFLOPS, 2),
         "peak_basis": f"MI355X dense {wl.in_dtype} MFMA 256 CU x 4096 FLOP/clk x 2.4 GHz = 2516.6 TFLOP/s",
+        "timing": {
+            "protocol": f"{len(t['burst_sizes'])} bursts of {t['burst_sizes'][0]} back-to-back launches after "
+                        f"{args.warmup} warm-up launches, HIP events on the launch stream; ms_per_step = "
+                        f"median burst (warm L2/MALL)",
+            "burst_ms_per_launch": [round(x, 5) for x in t["burst_ms_per_launch"]],
+            "ms_p10": round(t["p10"], 5),
+            "ms_p90": round(t["p90"], 5),
+            "ms_mean": round(t["mean"], 5),
+            "tflops_p10_p90": [tf(t["p90"]), tf(t["p10"])],
+            "cold_ms_median": round(percentile(cold, 50.0), 5) if cold else None,
+            "cold_tflops": tf(percentile(cold, 50.0)) if cold else None,
+            "cold_protocol": f"{len(cold)} launches, each after a 1 GiB scrub (inputs evicted from L2 and MALL), "
+                             f"median" if cold else None,
+        },
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),
@@ -343,7 +457,6 @@ def main() -> int:
         line["cpu_baseline"] = cpu_baseline(wl, q, k, v, out, scale)
     print(json.dumps(line), flush=True)
     return 0
-
 
 if __name__ == "__main__":
     sys.exit(main())
