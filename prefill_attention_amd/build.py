@@ -10,6 +10,7 @@ the planner is plain C++.  Packed-FP32 VALU forms are disabled for the device co
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -33,7 +34,43 @@ def _hipcc() -> str:
 
 def _run(cmd):
     print("+", " ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    sys.stdout.write(r.stdout)
+    if r.returncode:
+        sys.stderr.write(r.stderr)
+        raise subprocess.CalledProcessError(r.returncode, cmd)
+    return r.stderr
+
+
+def kernel_resources(remarks: str) -> dict:
+    """Per-kernel register, scratch and occupancy figures from hipcc's
+    -Rpass-analysis=kernel-resource-usage remarks: {name: {field: value}}."""
+    out, cur = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            out[cur] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[a-z/A-Z]+\])?: (\d+)", line)
+        if m and cur is not None:
+            out[cur][m.group(1).strip()] = int(m.group(2))
+    return out
+
+
+def check_resources(resources: dict) -> None:
+    """Fail the build when a shipped kernel spills or uses scratch memory.
+
+    A spill silently turns register traffic into memory traffic; like any
+    resource limit of the launch it must stop the build rather than ship a
+    slower kernel (the pages' rule that resource limits fail loudly).
+    """
+    bad = {name: r for name, r in resources.items()
+           if r.get("ScratchSize", 0) or r.get("VGPRs Spill", 0) or r.get("SGPRs Spill", 0)}
+    if bad:
+        lines = [f"  {n}: ScratchSize={r.get('ScratchSize')} VGPRs Spill={r.get('VGPRs Spill')} "
+                 f"SGPRs Spill={r.get('SGPRs Spill')}" for n, r in bad.items()]
+        raise RuntimeError("kernels with register spills or scratch memory:\n" + "\n".join(lines))
 
 
 HIP_SOURCES = ("fa_prefill.hip", "fa_prefill_hd64.hip", "fa_prefill_hd128.hip", "fa_prefill_hd256.hip",
@@ -41,7 +78,7 @@ HIP_SOURCES = ("fa_prefill.hip", "fa_prefill_hd64.hip", "fa_prefill_hd128.hip", 
 
 
 def build(verbose_resources: bool = False) -> str:
-    """Compile the library; return its path."""
+    """Compile the library; return its path.  Fails if any kernel spills."""
     from concurrent.futures import ThreadPoolExecutor
 
     hipcc = _hipcc()
@@ -56,8 +93,7 @@ def build(verbose_resources: bool = False) -> str:
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-ffp-contract=fast",
     ]
-    if verbose_resources:
-        dev_flags += ["-Rpass-analysis=kernel-resource-usage"]
+    dev_flags += ["-Rpass-analysis=kernel-resource-usage"]
     jobs = [[cxx, *common, "-c", os.path.join(CSRC, "fa_plan.cpp"), "-o", plan_o]]
     objs = [plan_o]
     for src in HIP_SOURCES:
@@ -65,13 +101,33 @@ def build(verbose_resources: bool = False) -> str:
         jobs.append([hipcc, *common, *dev_flags, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    resources = {}
     with ThreadPoolExecutor(max_workers=workers) as ex:
         for f in [ex.submit(_run, cmd) for cmd in jobs]:
-            f.result()
+            resources.update(kernel_resources(f.result()))
+    if verbose_resources:
+        for name, r in sorted(resources.items()):
+            print(f"{name}: {r}")
+    check_resources(resources)
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)
+    build_probes(hipcc, common, dev_flags)
     return LIB_PATH
+
+
+PROBE_SRC = os.path.join(ROOT, "tests", "probes", "fa_probes.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "probes", "libfa_probes.so")
+
+
+def build_probes(hipcc, common, dev_flags) -> None:
+    """The GPU tests' single-instruction layout probes (test infrastructure,
+    not part of the library): tests/probes/libfa_probes.so."""
+    if not os.path.exists(PROBE_SRC):
+        return
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc, *common, *[f for f in dev_flags if not f.startswith("-Rpass")], "-shared", PROBE_SRC, "-o", tmp])
+    os.replace(tmp, PROBE_LIB)
 
 
 if __name__ == "__main__":

@@ -62,8 +62,9 @@
 //    §3.2).
 //
 //  * Work-group order: the heaviest query tiles first; when the head count is
-//    a multiple of 8, the 8 XCDs (which receive work-groups round-robin) each
-//    own a contiguous range of heads, so one kv head's K/V stays in one L2,
+//    a multiple of 8, the 8 XCDs (which receive work-groups round-robin, so
+//    indices equal mod 8 share one) each own a contiguous range of heads, so
+//    one kv head's K/V stays in one L2,
 //    and an unsplit causal launch reverses the second half of each XCD's
 //    first dispatch wave so that heavy and light query tiles share CUs.
 #pragma once
@@ -169,9 +170,10 @@ struct Tile {
 };
 
 // max / sum of x over the lane pair (lane, lane ^ 32).  v_permlane32_swap
-// exchanges the upper half of its first operand with the lower half of its
-// second; with both operands = x the two results hold x and the partner
-// lane's x, in some order, in every lane.
+// exchanges the upper 32 lanes of its first operand with the lower 32 lanes
+// of its second; with both operands = x, every lane l receives x[l % 32] as
+// the first result and x[l % 32 + 32] as the second (a single-instruction
+// GPU test checks this), so the pair's two values are both in every lane.
 __device__ __forceinline__ float pair_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -185,6 +187,19 @@ __device__ __forceinline__ float pair_sum(float x) {
 // lane group g: the 32x32 MFMA result row index.
 __device__ __forceinline__ int acc_key(int kb, int i, int g) {
     return 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+}
+
+// K fragment (kb, t) of a staged key tile: the A operand of S^T block kb at
+// k-step t, i.e. key row 32 kb + l32 and head-dim columns 16 t + 8 g .. +8,
+// stored as logical chunk 2 t + g of that row at physical chunk
+// (2 t + g) ^ swz(l32) (swz(32 kb + l32) == swz(l32)).  `row` is the tile
+// plus l32 rows and z = swz(l32).  The permutation only touches the low 4
+// bits of the chunk, so fragments t and t + 8 are 256 bytes apart: 8
+// per-lane addresses, the rest immediate offsets.
+template <int HD, typename T>
+__device__ __forceinline__ typename Operand<T>::x8 load_k_frag(const char* row, int z, int g, int kb, int t) {
+    return *reinterpret_cast<const typename Operand<T>::x8*>(row + kb * 32 * Tile<HD>::kRowBytes + (t >> 3) * 256 +
+                                                             (((2 * (t & 7) + g) ^ z) << 4));
 }
 
 // Copy key/value rows [kt, kt + 64) of head hk into an LDS tile; head_base
@@ -325,18 +340,9 @@ __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
     using X2 = typename Op::x2;
     constexpr int kSlots = 2 * L::kQFrags;
     float lsum = 0.0f;
-    // K fragment (kb, t): key row 32kb + l32, head-dim 16t + 8g, i.e. logical
-    // chunk 2t + g at physical chunk (2t + g) ^ swz(l32) (swz(32kb + l32) ==
-    // swz(l32)).  The permutation only touches the low 4 bits of the chunk,
-    // so fragments t and t + 8 are 256 bytes apart: 8 per-lane addresses,
-    // the rest immediate offsets.
     const int z = L::swz(l32);
     const char* rp = ktile_next + l32 * L::kRowBytes;
-    auto kread = [&](int i) {
-        const int kb = i / L::kQFrags, t = i % L::kQFrags;
-        return *reinterpret_cast<const X8*>(rp + kb * 32 * L::kRowBytes + (t >> 3) * 256 +
-                                            (((2 * (t & 7) + g) ^ z) << 4));
-    };
+    auto kread = [&](int i) { return load_k_frag<HD, T>(rp, z, g, i / L::kQFrags, i % L::kQFrags); };
     // VALU chunk c: probabilities 2c and 2c + 1 of the current tile.
     auto valu_chunk = [&](int c) {
         const int kb = c >> 3, e = 2 * (c & 7);
@@ -487,13 +493,16 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     const int g = lane >> 5;
 
     // Work-group -> (head, query tile, key-range part), heaviest query tiles
-    // first.  Work-groups are dispatched round-robin over the XCDs (XCD x =
-    // blockIdx % 8), and all parts of a split query tile must meet in one
-    // XCD's L2.  With a head count divisible by 8, XCD x owns heads
-    // [x*H/8, (x+1)*H/8), so one kv head's K/V also stays in one L2.  Other
-    // head counts deal the items (rank * H + head, heaviest first) round-robin
-    // over the XCDs, the parts of item i on XCD i % 8; the grid is padded to a
-    // multiple of 8 items, and padding work-groups exit at once.
+    // first.  Work-groups are dispatched round-robin over the XCDs, starting
+    // at an XCD that varies from launch to launch: work-groups whose indices
+    // agree mod 8 run on one XCD (a single-instruction GPU test reads the
+    // XCC_ID register to check it), and all parts of a split query tile must
+    // meet in one XCD's L2.  With a head count divisible by 8, residue x owns
+    // heads [x*H/8, (x+1)*H/8), so one kv head's K/V also stays in one L2.
+    // Other head counts deal the items (rank * H + head, heaviest first)
+    // round-robin over the residues, the parts of item i on residue i % 8;
+    // the grid is padded to a multiple of 8 items, and padding work-groups
+    // exit at once.
     const int b = blockIdx.x;
     int h, rank, split = 0;
     if ((n_q_heads % kXcds) == 0) {
@@ -629,6 +638,10 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
         phase_b<HD, TI, false>(vbuf(j), pb, oacc, sc, c2, l32, g, vt_off, vf);
     };
 
+    // One copy of the last tile's code: with an even tile count the odd step
+    // leaves its scores in sb, copied to sa once.  (Two inlined copies of
+    // last(), one per score buffer, made the register allocator shuffle the
+    // accumulators at the merge and spill.)
     int j = 0;
     for (; j + 2 < n_tiles; j += 2) {
         step(j, sa, sb);
@@ -636,10 +649,10 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     }
     if (j + 1 < n_tiles) {
         step(j, sa, sb);
-        last(j + 1, sb);
-    } else {
-        last(j, sa);
+        sa = sb;
+        ++j;
     }
+    last(j, sa);
 
     // Epilogue, rows < q_len only.  Lane (l32, g), register i of block db
     // holds head-dim 32*db + 8*(i/4) + 4*g + i%4.
@@ -704,7 +717,7 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
             ws_lw[(part0 + split) * kQTile + row] =
                 l_tot > 0.0f ? m_ref + __builtin_amdgcn_logf(l_tot) : -INFINITY;
     }
-    // All parts of this tile run on this XCD and meet in its L2: each wave
+    // All parts of this tile run on one XCD and meet in its L2: each wave
     // waits until its stores have reached the L2 before the arrival is
     // counted (an atomic performed in the L2), and the last part drops its
     // CU's L1 lines before reading the others' results.

@@ -1,0 +1,78 @@
+"""Host tests of the build's resource check, the bench's timing helpers and
+the headline path's no-allocation property (no GPU)."""
+
+from __future__ import annotations
+
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import prefill_attention_amd as fa  # noqa: E402
+from prefill_attention_amd import build  # noqa: E402
+from prefill_attention_amd.workloads import WORKLOADS  # noqa: E402
+
+REMARKS = """\
+k.h:469:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]
+k.h:469:1: remark:     TotalSGPRs: 78 [-Rpass-analysis=kernel-resource-usage]
+k.h:469:1: remark:     VGPRs: 250 [-Rpass-analysis=kernel-resource-usage]
+k.h:469:1: remark:     AGPRs: 0 [-Rpass-analysis=kernel-resource-usage]
+k.h:469:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]
+k.h:469:1: remark:     Occupancy [waves/SIMD]: 2 [-Rpass-analysis=kernel-resource-usage]
+k.h:469:1: remark:     SGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+k.h:469:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+k.h:469:1: remark:     LDS Size [bytes/block]: 65552 [-Rpass-analysis=kernel-resource-usage]
+k.h:469:1: remark: Function Name: kern_b [-Rpass-analysis=kernel-resource-usage]
+k.h:469:1: remark:     VGPRs: 256 [-Rpass-analysis=kernel-resource-usage]
+k.h:469:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]
+k.h:469:1: remark:     VGPRs Spill: 2 [-Rpass-analysis=kernel-resource-usage]
+"""
+
+
+def test_kernel_resource_remarks_parsed():
+    r = build.kernel_resources(REMARKS)
+    assert r["kern_a"]["VGPRs"] == 250 and r["kern_a"]["ScratchSize"] == 0
+    assert r["kern_a"]["Occupancy"] == 2 and r["kern_a"]["LDS Size"] == 65552
+    assert r["kern_b"]["VGPRs Spill"] == 2 and r["kern_b"]["ScratchSize"] == 12
+
+
+def test_build_fails_on_spills_and_scratch():
+    r = build.kernel_resources(REMARKS)
+    build.check_resources({"kern_a": r["kern_a"]})
+    with pytest.raises(RuntimeError, match="kern_b"):
+        build.check_resources(r)
+    with pytest.raises(RuntimeError):
+        build.check_resources({"k": {"ScratchSize": 16, "VGPRs Spill": 0}})
+
+
+@pytest.mark.parametrize("steps,bursts,want", [
+    (350, 7, [50] * 7), (20, 7, [3, 3, 3, 3, 3, 3, 2]), (3, 7, [1, 1, 1]), (1, 7, [1]), (10, 1, [10]),
+])
+def test_burst_split_covers_every_step(steps, bursts, want):
+    assert bench.burst_split(steps, bursts) == want
+    assert sum(bench.burst_split(steps, bursts)) == steps
+
+
+def test_percentile():
+    xs = [5.0, 1.0, 3.0, 2.0, 4.0]
+    assert bench.percentile(xs, 50) == 3.0
+    assert bench.percentile(xs, 0) == 1.0 and bench.percentile(xs, 100) == 5.0
+    assert bench.percentile(xs, 10) == pytest.approx(1.4)
+    assert bench.percentile([7.0], 90) == 7.0
+
+
+@pytest.mark.parametrize("key", ["tiny", "7b_2k", "7b_2659", "gqa_4k", "long_16k"])
+def test_five_configs_never_split_nor_allocate(key):
+    """The five benchmark configurations plan no split, hence no workspace:
+    the headline path allocates nothing and keeps no state."""
+    wl = WORKLOADS[key]
+    p = fa.fa_prefill_plan(wl.n_q_heads, wl.n_kv_heads, wl.seq_len, wl.head_dim, int(wl.causal))
+    if key == "tiny":
+        # 4 query tiles under-fill the device, but each is too short to split
+        assert p.n_q_tiles * wl.n_q_heads * 2 <= 512
+    assert p.kv_splits == 1
+    assert p.workspace_bytes == 0
