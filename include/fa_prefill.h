@@ -57,8 +57,11 @@
  * synchronising that stream), and kept until fa_prefill_free_workspaces.
  * Calls on one stream use it in stream order; calls on different streams
  * never share a block.  A call that needs a new or larger block must
- * therefore not be made during HIP graph capture.  Whole-sequence prefills
- * that fill the device never split and never allocate.
+ * therefore not be made during HIP graph capture, and a graph captured with
+ * a block keeps that block's address: growing it (a later, larger split
+ * call on the same stream) or fa_prefill_free_workspaces frees that memory,
+ * after which the graph must not be replayed.  Whole-sequence prefills that
+ * fill the device never split and never allocate.
  *
  * Execution.  fa_prefill enqueues one kernel on `stream` (a hipStream_t;
  * NULL = the null stream) and returns without waiting; the caller
@@ -67,7 +70,11 @@
  * Errors.  Every function returns an fa_status; no call falls back to
  * another code path.  Argument errors are detected on the host before any
  * GPU call.  fa_prefill_last_error() gives a detail message for the last
- * failing call on the calling thread.
+ * failing call on the calling thread.  (The pages' launcher returns an int
+ * status and derives its launch resources from the tile constants — "49 ·
+ * r46 (FAP1) — FA audit", §3.2 — and a request the hardware cannot meet must
+ * fail loudly instead of silently running something else — "11 · P5 —
+ * prefill gap session", §3.3 and its first lesson.)
  */
 #ifndef FA_PREFILL_H
 #define FA_PREFILL_H
@@ -76,6 +83,10 @@
 extern "C" {
 #endif
 
+/* Status of every entry point: an int-returning launcher, as the pages' own
+ * ("49 · r46 (FAP1) — FA audit", §3.2), where each way a call can be refused
+ * has its own code and nothing falls back to another path ("11 · P5 —
+ * prefill gap session", §3.3, first lesson). */
 typedef enum fa_status {
     FA_OK = 0,            /* success (seq_len / q_len == 0 is a successful no-op) */
     FA_ERR_NULL = 1,      /* q, k, v or out is NULL (with seq_len > 0)             */
@@ -197,7 +208,9 @@ int fa_prefill_chunk_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, 
  */
 int fa_prefill_free_workspaces(void);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
+/* Static, NUL-terminated description of a status code (never NULL): the
+ * loud failure the pages ask of a launch that cannot run as requested ("11 ·
+ * P5 — prefill gap session", §3.3, first lesson), in words. */
 const char* fa_prefill_strerror(int status);
 
 /* Detail of the last error on the calling thread ("" if none); valid until the

@@ -71,9 +71,12 @@ struct Workspace {
     float* o;
 };
 
+// The caller holds g_ws_mu from here until its kernel launch has been
+// enqueued, so a concurrent call that grows the block, or
+// fa_prefill_free_workspaces, cannot free it before this launch is on its
+// stream (both wait for the stream or device before freeing).
 int acquire_workspace(int dev, void* stream, long long items, long long parts, long long o_floats,
                       Workspace* ws) {
-    std::lock_guard<std::mutex> lk(g_ws_mu);
     WorkspaceBlock* blk = nullptr;
     for (WorkspaceBlock& w : g_ws)
         if (w.dev == dev && w.stream == stream) blk = &w;
@@ -144,8 +147,12 @@ int launch(const void* q, const void* k, const void* v, void* out, int n_q_heads
     if (st != FA_OK) return st;
     Workspace ws{nullptr, nullptr, nullptr};
     int n_splits = plan.kv_splits;
+    const long long items = (long long)plan.n_q_tiles * n_q_heads;
+    // Held from the workspace lookup until the launch is enqueued (split
+    // launches only).
+    std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
     if (n_splits > 1) {
-        const long long items = (long long)plan.n_q_tiles * n_q_heads;
+        ws_lock.lock();
         st = acquire_workspace(dev, stream, items, items * n_splits,
                                items * n_splits * (long long)kQTile * head_dim, &ws);
         if (st != FA_OK) return st;
