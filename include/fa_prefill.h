@@ -60,8 +60,9 @@
  * therefore not be made during HIP graph capture, and a graph captured with
  * a block keeps that block's address: growing it (a later, larger split
  * call on the same stream) or fa_prefill_free_workspaces frees that memory,
- * after which the graph must not be replayed.  Whole-sequence prefills that
- * fill the device never split and never allocate.
+ * after which the graph must not be replayed.  Callers that cannot allocate
+ * at all use fa_prefill_ex_noalloc.  Whole-sequence prefills that fill the
+ * device never split and never allocate.
  *
  * Execution.  fa_prefill enqueues one kernel on `stream` (a hipStream_t;
  * NULL = the null stream) and returns without waiting; the caller
@@ -185,6 +186,27 @@ int fa_prefill_chunk(const void* q, const void* k, const void* v, float* out,
 int fa_prefill_ex(const void* q, const void* k, const void* v, void* out,
                   int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim,
                   float scale, int causal, int in_dtype, int out_dtype, void* stream);
+
+/*
+ * fa_prefill_ex without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, layouts, results and errors as
+ * fa_prefill_ex; the outputs are bitwise those of fa_prefill_ex for the same
+ * inputs.  A split launch (fa_plan.kv_splits > 1) takes its workspace from a
+ * static device array of the library, 34 MiB per GPU, held until the process
+ * ends, instead of a library-owned block: enough for every split the planner
+ * makes on an MI355X (fa_plan.workspace_bytes is at most about 33 MiB there);
+ * a plan needing more returns FA_ERR_WORKSPACE.  Before a split launch it
+ * enqueues one small kernel that zeroes the array's arrival counters (no
+ * memset).  The first call on a device resolves that device's array address
+ * (FA_ERR_WORKSPACE if that fails).  It never calls hipMalloc or hipFree.
+ * Calls on one GPU share its array: two split calls that may overlap in time
+ * on one GPU (different streams without ordering between them) race and give
+ * wrong results; calls ordered on one stream are safe.
+ */
+int fa_prefill_ex_noalloc(const void* q, const void* k, const void* v, void* out,
+                          int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim,
+                          float scale, int causal, int in_dtype, int out_dtype, void* stream);
 
 /*
  * Compute the launch plan fa_prefill would use, without touching the GPU, for

@@ -16,6 +16,7 @@ from .binding import (
     fa_prefill_chunk,
     fa_prefill_chunk_plan,
     fa_prefill_ex,
+    fa_prefill_ex_noalloc,
     fa_prefill_free_workspaces,
     fa_prefill_last_error,
     fa_prefill_plan,
@@ -36,6 +37,7 @@ __all__ = [
     "fa_prefill_chunk",
     "fa_prefill_chunk_plan",
     "fa_prefill_ex",
+    "fa_prefill_ex_noalloc",
     "fa_prefill_free_workspaces",
     "fa_prefill_last_error",
     "fa_prefill_plan",

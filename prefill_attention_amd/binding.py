@@ -32,7 +32,8 @@ STATUS_NAMES = {
 FA_DTYPE_F16, FA_DTYPE_BF16, FA_DTYPE_F32 = 0, 1, 2
 HEAD_DIMS = (64, 128, 256)
 # Every symbol include/fa_prefill.h and include/fa_kv_store.h declare.
-EXPORTED = ("fa_prefill", "fa_prefill_chunk", "fa_prefill_ex", "fa_prefill_plan", "fa_prefill_chunk_plan",
+EXPORTED = ("fa_prefill", "fa_prefill_chunk", "fa_prefill_ex", "fa_prefill_ex_noalloc", "fa_prefill_plan",
+            "fa_prefill_chunk_plan",
             "fa_prefill_free_workspaces", "fa_prefill_strerror", "fa_prefill_last_error",
             "fa_store_kv", "fa_convert_f16")
 
@@ -102,6 +103,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
         ]
+        lib.fa_prefill_ex_noalloc.restype = ctypes.c_int
+        lib.fa_prefill_ex_noalloc.argtypes = lib.fa_prefill_ex.argtypes
         lib.fa_prefill_chunk_plan.restype = ctypes.c_int
         lib.fa_prefill_chunk_plan.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -160,6 +163,15 @@ def fa_prefill_ex(q, k, v, out, n_q_heads: int, n_kv_heads: int, q_len: int, kv_
     lib = load_library()
     return lib.fa_prefill_ex(q, k, v, out, int(n_q_heads), int(n_kv_heads), int(q_len), int(kv_len),
                              int(head_dim), float(scale), int(causal), int(in_dtype), int(out_dtype), stream)
+
+
+def fa_prefill_ex_noalloc(q, k, v, out, n_q_heads: int, n_kv_heads: int, q_len: int, kv_len: int,
+                          head_dim: int, scale: float, causal: int, in_dtype: int, out_dtype: int, stream) -> int:
+    """Same arguments as the C function; pointers as ints (or None), returns the status."""
+    lib = load_library()
+    return lib.fa_prefill_ex_noalloc(q, k, v, out, int(n_q_heads), int(n_kv_heads), int(q_len), int(kv_len),
+                                     int(head_dim), float(scale), int(causal), int(in_dtype), int(out_dtype),
+                                     stream)
 
 
 def fa_prefill_chunk_plan(n_q_heads: int, n_kv_heads: int, q_len: int, kv_len: int, head_dim: int,

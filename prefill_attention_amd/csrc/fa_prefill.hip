@@ -116,6 +116,53 @@ int acquire_workspace(int dev, void* stream, long long items, long long parts, l
     return FA_OK;
 }
 
+// Workspace of fa_prefill_ex_noalloc: one static device array per GPU,
+// sized for the largest split launch the planner makes on a 256-CU device
+// (at most 512 parts of 128 query rows; head_dim 256 has 256 parts): the
+// counters of up to 256 items, the log-weights and the partial outputs.
+// In host code `scratch` is only a stand-in for the symbol; its device
+// address, one per GPU, comes from hipGetSymbolAddress.
+constexpr long long kScratchBytes = 34ll << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+char* g_scratch_ptr[kMaxDevices];
+int g_scratch_state[kMaxDevices];  // 0 unknown, 1 resolved, else the failure status
+std::mutex g_scratch_mu;
+
+// Device address of this GPU's scratch array, resolved once per device with
+// the device current (the caller made it current).
+int scratch_address(int dev, char** ptr) {
+    int st = __atomic_load_n(&g_scratch_state[dev], __ATOMIC_ACQUIRE);
+    if (st == 1) {
+        *ptr = g_scratch_ptr[dev];
+        return FA_OK;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    st = g_scratch_state[dev];
+    if (st == 0) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            g_scratch_state[dev] = FA_ERR_WORKSPACE;
+            return fail(FA_ERR_WORKSPACE, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = static_cast<char*>(p);
+        __atomic_store_n(&g_scratch_state[dev], 1, __ATOMIC_RELEASE);
+        st = 1;
+    }
+    if (st != 1) return fail(st, "the scratch array of device %d is unusable (see first error)", dev);
+    *ptr = g_scratch_ptr[dev];
+    return FA_OK;
+}
+
+// Zero n ints (the split launch's arrival counters): a kernel rather than a
+// memset, so that a caller may capture the call in a HIP graph.
+__global__ void zero_ints(int* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
 }  // namespace
 }  // namespace fa
 
@@ -123,9 +170,11 @@ namespace fa {
 namespace {
 
 // Every entry point: q_len queries at the last q_len of kv_len positions.
+// no_alloc: take the split workspace from the static scratch array instead of
+// the library-owned blocks (fa_prefill_ex_noalloc).
 int launch(const void* q, const void* k, const void* v, void* out, int n_q_heads, int n_kv_heads,
            int q_len, int kv_len, int head_dim, float scale, int causal, int in_dtype, int out_dtype,
-           void* stream) {
+           void* stream, bool no_alloc) {
     clear_error();
     fa_plan plan;
     int st = check_dtypes(in_dtype, out_dtype);
@@ -149,9 +198,27 @@ int launch(const void* q, const void* k, const void* v, void* out, int n_q_heads
     int n_splits = plan.kv_splits;
     const long long items = (long long)plan.n_q_tiles * n_q_heads;
     // Held from the workspace lookup until the launch is enqueued (split
-    // launches only).
+    // launches on library-owned blocks only).
     std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
-    if (n_splits > 1) {
+    if (n_splits > 1 && no_alloc) {
+        if (plan.workspace_bytes > kScratchBytes)
+            return fail(FA_ERR_WORKSPACE, "split launch needs %lld B of workspace; the scratch array holds %lld B",
+                        plan.workspace_bytes, kScratchBytes);
+        char* base = nullptr;
+        st = scratch_address(dev, &base);
+        if (st != FA_OK) return st;
+        // Laid out for this plan: counters, log-weights, partial outputs.
+        ws.ctr = reinterpret_cast<int*>(base);
+        ws.lw = reinterpret_cast<float*>(base + workspace_lw_offset(items));
+        ws.o = reinterpret_cast<float*>(base + workspace_o_offset(items, items * n_splits));
+        // The array keeps the previous call's contents; the counters must
+        // start at zero.
+        const int n = (int)items;
+        hipLaunchKernelGGL(zero_ints, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), ws.ctr, n);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "counter reset: %s", hipGetErrorString(e));
+    } else if (n_splits > 1) {
         ws_lock.lock();
         st = acquire_workspace(dev, stream, items, items * n_splits,
                                items * n_splits * (long long)kQTile * head_dim, &ws);
@@ -192,7 +259,7 @@ extern "C" int fa_prefill(const void* q, const void* k, const void* v, float* ou
                           int n_kv_heads, int seq_len, int head_dim, float scale, int causal,
                           void* stream) {
     return fa::launch(q, k, v, out, n_q_heads, n_kv_heads, seq_len, seq_len, head_dim, scale, causal,
-                      FA_DTYPE_F16, FA_DTYPE_F32, stream);
+                      FA_DTYPE_F16, FA_DTYPE_F32, stream, false);
 }
 
 extern "C" int fa_prefill_free_workspaces(void) {
@@ -217,12 +284,19 @@ extern "C" int fa_prefill_chunk(const void* q, const void* k, const void* v, flo
                                 int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim,
                                 float scale, int causal, void* stream) {
     return fa::launch(q, k, v, out, n_q_heads, n_kv_heads, q_len, kv_len, head_dim, scale, causal,
-                      FA_DTYPE_F16, FA_DTYPE_F32, stream);
+                      FA_DTYPE_F16, FA_DTYPE_F32, stream, false);
 }
 
 extern "C" int fa_prefill_ex(const void* q, const void* k, const void* v, void* out, int n_q_heads,
                              int n_kv_heads, int q_len, int kv_len, int head_dim, float scale,
                              int causal, int in_dtype, int out_dtype, void* stream) {
     return fa::launch(q, k, v, out, n_q_heads, n_kv_heads, q_len, kv_len, head_dim, scale, causal,
-                      in_dtype, out_dtype, stream);
+                      in_dtype, out_dtype, stream, false);
+}
+
+extern "C" int fa_prefill_ex_noalloc(const void* q, const void* k, const void* v, void* out, int n_q_heads,
+                                     int n_kv_heads, int q_len, int kv_len, int head_dim, float scale,
+                                     int causal, int in_dtype, int out_dtype, void* stream) {
+    return fa::launch(q, k, v, out, n_q_heads, n_kv_heads, q_len, kv_len, head_dim, scale, causal,
+                      in_dtype, out_dtype, stream, true);
 }

@@ -76,3 +76,21 @@ def test_five_configs_never_split_nor_allocate(key):
         assert p.n_q_tiles * wl.n_q_heads * 2 <= 512
     assert p.kv_splits == 1
     assert p.workspace_bytes == 0
+
+
+def test_noalloc_scratch_covers_every_split_plan():
+    """fa_prefill_ex_noalloc's static workspace (34 MiB) holds every split the
+    planner makes for a 256-CU device: at most 512 parts (256 for head_dim
+    256) of 128 rows, with their log-weights and the counters of <= 256 items."""
+    scratch = 34 << 20
+    worst = 0
+    for hd in (64, 128, 256):
+        for nq, nkv in ((1, 1), (2, 1), (3, 3), (4, 2), (6, 2), (8, 8), (16, 4), (28, 4), (32, 8), (64, 8),
+                        (96, 8), (128, 8), (256, 8)):
+            for q_len, kv_len in ((1, 1200), (1, 4096), (1, 131072), (16, 8192), (64, 9000), (128, 16384),
+                                  (256, 20000), (512, 65536), (1024, 131072), (2659, 2659), (16384, 16384),
+                                  (65536, 65536)):
+                p = fa.fa_prefill_chunk_plan(nq, nkv, q_len, kv_len, hd, 1)
+                worst = max(worst, p.workspace_bytes)
+                assert p.workspace_bytes <= scratch, (hd, nq, nkv, q_len, kv_len, p.workspace_bytes)
+    assert worst > 16 << 20  # the sweep reaches the large splits
