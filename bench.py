@@ -303,6 +303,9 @@ def main() -> int:
     ap.add_argument("--workload", default=None,
                     help="workload key (default: the headline one; 'all': one line per configuration)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--lib", default=None, metavar="PATH",
+                    help="time this build of libfa_prefill.so (e.g. another tile geometry from "
+                         "prefill_attention_amd.build --kv-tile/--waves/--out) instead of the in-tree one")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of attention, run --steps device-to-device copies of MIB MiB "
                          "(reference for scaling HBM byte counters)")
@@ -336,6 +339,10 @@ def main() -> int:
         return 0
     from prefill_attention_amd.workloads import STORE_WORKLOADS
 
+    if args.lib:
+        import prefill_attention_amd as fa
+
+        fa.load_library(os.path.abspath(args.lib))
     key = args.workload or HEADLINE
     if key in STORE_WORKLOADS:
         return store_bench(args, key)
@@ -407,7 +414,7 @@ def attention_bench(args, key) -> int:
     tflops = wl.flop / (ms_per_step * 1e-3) / 1e12
     tf = lambda ms: round(wl.flop / (ms * 1e-3) / 1e12, 2)  # noqa: E731
 
-    traffic = measured_traffic(key)
+    traffic = measured_traffic(key) if not args.lib else None  # the record is the shipped build's
     min_bytes = (q.numel() + k.numel() + v.numel()) * 2 + out.numel() * out.element_size()
     line = {
         "metric": "causal FA prefill TFLOP/s + % f16 MFMA peak (S=2659, 32 heads, hd=128)"
@@ -423,7 +430,8 @@ def attention_bench(args, key) -> int:
         "vs_baseline": None,
         "dtype": wl.in_dtype,
         "data": "synthetic",
-        "config": {**wl.describe(), "workload_key": key, "plan": plan.as_dict()},
+        "config": {**wl.describe(), "workload_key": key, "plan": plan.as_dict(),
+                   **({"library": os.path.abspath(args.lib)} if args.lib else {})},
         "pct_peak": round(100.0 * tflops / PEAK_F16_TFLOPS, 2),
         "peak_basis": f"MI355X dense {wl.in_dtype} MFMA 256 CU x 4096 FLOP/clk x 2.4 GHz = 2516.6 TFLOP/s",
         "timing": {

@@ -70,15 +70,21 @@ class FaError(RuntimeError):
 
 
 _lib = None
+_lib_path = None
 _lock = threading.Lock()
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libfa_prefill.so once; raise if it has not been built."""
-    global _lib
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libfa_prefill.so once (the in-tree build unless `path` names
+    another build); raise if it has not been built, or if a different build
+    was loaded earlier in this process."""
+    global _lib, _lib_path
     with _lock:
         if _lib is not None:
+            if path is not None and os.path.abspath(path) != _lib_path:
+                raise RuntimeError(f"{_lib_path} is already loaded; cannot switch to {path}")
             return _lib
+        path = os.path.abspath(path) if path is not None else LIB_PATH
         if not os.path.exists(path):
             raise FileNotFoundError(
                 f"{path} is missing: build it with `python -m prefill_attention_amd.build` "
@@ -131,6 +137,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_convert_f16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong,
                                        ctypes.c_void_p]
         _lib = lib
+        _lib_path = path
         return lib
 
 

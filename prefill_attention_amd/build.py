@@ -1,6 +1,9 @@
 """Build libfa_prefill.so in-tree for gfx950 with hipcc.
 
     python -m prefill_attention_amd.build        # or __graft_entry__.build()
+    python -m prefill_attention_amd.build --kv-tile 32 --waves 4
+                       # another tile geometry, for measurement, into
+                       # prefill_attention_amd/geometry/kv32_w4/libfa_prefill.so
 
 The HIP translation units (the attention's host launcher, one kernel unit per
 head dimension, the K/V producer) are compiled for gfx950 only, in parallel;
@@ -77,14 +80,36 @@ HIP_SOURCES = ("fa_prefill.hip", "fa_prefill_hd64.hip", "fa_prefill_hd128.hip", 
                "fa_kv_store.hip")
 
 
-def build(verbose_resources: bool = False) -> str:
-    """Compile the library; return its path.  Fails if any kernel spills."""
+SHIPPED_GEOMETRY = (64, 4)  # (key/value tile rows, wavefronts per work-group)
+
+
+def geometry_lib_path(kv_tile: int, waves: int) -> str:
+    """Where a build of another tile geometry goes by default (bench.py --lib)."""
+    return os.path.join(PKG, "geometry", f"kv{kv_tile}_w{waves}", LIB_NAME)
+
+
+def build(verbose_resources: bool = False, kv_tile: int = 64, waves: int = 4, out: str | None = None,
+          allow_spills: bool = False) -> str:
+    """Compile the library; return its path.  Fails if any kernel spills.
+
+    kv_tile / waves select another tile geometry (FA_KV_TILE in {32, 64,
+    128}, FA_WAVES in {4, 8}) for measuring it; such a build goes to `out`
+    or geometry_lib_path() and never replaces the shipped library.  allow_spills lets a
+    geometry whose register budget overflows build anyway (for measurement
+    only; the shipped geometry never spills).
+    """
     from concurrent.futures import ThreadPoolExecutor
 
+    shipped = (kv_tile, waves) == SHIPPED_GEOMETRY
+    lib_path = os.path.abspath(out) if out else (LIB_PATH if shipped else geometry_lib_path(kv_tile, waves))
+    build_dir = BUILD_DIR if shipped else os.path.join(BUILD_DIR, f"kv{kv_tile}_w{waves}")
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(lib_path), exist_ok=True)
     common = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
-    plan_o = os.path.join(BUILD_DIR, "fa_plan.o")
+    if not shipped:
+        common += [f"-DFA_KV_TILE={kv_tile}", f"-DFA_WAVES={waves}"]
+    plan_o = os.path.join(build_dir, "fa_plan.o")
     cxx = shutil.which("g++") or shutil.which("c++")
     if cxx is None:
         raise RuntimeError("a host C++ compiler (g++) is required")
@@ -97,7 +122,7 @@ def build(verbose_resources: bool = False) -> str:
     jobs = [[cxx, *common, "-c", os.path.join(CSRC, "fa_plan.cpp"), "-o", plan_o]]
     objs = [plan_o]
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         jobs.append([hipcc, *common, *dev_flags, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
@@ -108,12 +133,14 @@ def build(verbose_resources: bool = False) -> str:
     if verbose_resources:
         for name, r in sorted(resources.items()):
             print(f"{name}: {r}")
-    check_resources(resources)
-    tmp = LIB_PATH + ".tmp"
+    if not (allow_spills and not shipped):
+        check_resources(resources)
+    tmp = lib_path + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB_PATH)
-    build_probes(hipcc, common, dev_flags)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    if shipped:
+        build_probes(hipcc, common, dev_flags)
+    return lib_path
 
 
 PROBE_SRC = os.path.join(ROOT, "tests", "probes", "fa_probes.hip")
@@ -131,4 +158,14 @@ def build_probes(hipcc, common, dev_flags) -> None:
 
 
 if __name__ == "__main__":
-    build(verbose_resources="-v" in sys.argv)
+    import argparse
+
+    ap = argparse.ArgumentParser(description="build libfa_prefill.so for gfx950")
+    ap.add_argument("-v", action="store_true", help="print every kernel's register / scratch / LDS figures")
+    ap.add_argument("--kv-tile", type=int, default=SHIPPED_GEOMETRY[0], help="key/value rows per tile (32, 64, 128)")
+    ap.add_argument("--waves", type=int, default=SHIPPED_GEOMETRY[1], help="wavefronts per work-group (4, 8)")
+    ap.add_argument("--out", default=None, help="library path (default: in-tree; another geometry: "
+                                                "prefill_attention_amd/geometry/kv<T>_w<W>/)")
+    ap.add_argument("--allow-spills", action="store_true", help="build a spilling non-shipped geometry anyway")
+    a = ap.parse_args()
+    print(build(verbose_resources=a.v, kv_tile=a.kv_tile, waves=a.waves, out=a.out, allow_spills=a.allow_spills))

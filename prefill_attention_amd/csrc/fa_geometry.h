@@ -9,22 +9,30 @@
 
 namespace fa {
 
+// Key/value tile width and wavefronts per work-group are build-time
+// parameters (FA_KV_TILE in {32, 64, 128}, FA_WAVES in {4, 8}; build.py
+// --kv-tile / --waves).  The library ships 64 and 4: of the six
+// combinations, measured on every benchmark shape with rocprof counters
+// (MFMA-busy cycles, dependency waits, LDS bank conflicts, occupancy), it is
+// the fastest everywhere.
+#ifndef FA_KV_TILE
+#define FA_KV_TILE 64
+#endif
+#ifndef FA_WAVES
+#define FA_WAVES 4
+#endif
 constexpr int kWaveSize = 64;          // CDNA wavefront
 constexpr int kQRowsPerWave = 32;      // one 32x32 MFMA column block of queries
-constexpr int kWaves = 4;              // wavefronts per work-group
+constexpr int kWaves = FA_WAVES;       // wavefronts per work-group
 constexpr int kThreads = kWaves * kWaveSize;
-constexpr int kQTile = kWaves * kQRowsPerWave;  // 128 query rows per work-group
-constexpr int kKvTile = 64;            // key/value rows per LDS tile
+constexpr int kQTile = kWaves * kQRowsPerWave;  // query rows per work-group (128)
+constexpr int kKvTile = FA_KV_TILE;    // key/value rows per LDS tile (64)
+constexpr int kKb = kKvTile / 32;      // 32-key accumulator blocks per tile
+constexpr int kKs = kKvTile / 16;      // 16-key MFMA k-steps per tile
+static_assert(kKvTile == 32 || kKvTile == 64 || kKvTile == 128, "FA_KV_TILE must be 32, 64 or 128");
+static_assert(kWaves == 4 || kWaves == 8, "FA_WAVES must be 4 or 8");
 constexpr int kStages = 2;             // LDS tiles in flight (double buffer)
 
-// Head dimensions built: the pages' model uses 128 throughout; 64 and 256
-// are the same kernel with narrower or wider rows.
-constexpr bool head_dim_supported(int hd) { return hd == 64 || hd == 128 || hd == 256; }
-
-// Resident work-groups per CU: two (2 waves per SIMD, 256 registers each)
-// for head_dim <= 128; one for 256, whose 128 KiB of K/V planes and 8 output
-// blocks per wave need a whole CU's LDS and a SIMD's full register file.
-constexpr int groups_per_cu(int hd) { return hd > 128 ? 1 : 2; }
 
 // Split-KV for grids that would leave work-group slots idle (a short chunk over
 // a long KV cache, or a prefill of few heads): each query tile's key range is
@@ -49,9 +57,33 @@ constexpr int tile_bytes(int hd) { return kKvTile * row_bytes(hd); }   // one K 
 constexpr int lds_k_bytes(int hd) { return kStages * tile_bytes(hd); }
 constexpr int lds_v_bytes(int hd) { return kStages * tile_bytes(hd); }
 constexpr int kLdsMiscBytes = 16;                                       // the merge-election flag
-constexpr int lds_bytes(int hd) { return lds_k_bytes(hd) + lds_v_bytes(hd) + kLdsMiscBytes; }
-// 32 KiB + 16 B (64), 64 KiB + 16 B (128), 128 KiB + 16 B (256)
-constexpr int kLdsBytesMax = lds_bytes(256);
+// The epilogue reuses the planes to write each wave's 32 f32 output rows
+// row-major; a work-group needs the larger of the two.
+constexpr int lds_epilogue_bytes(int hd) { return kWaves * kQRowsPerWave * hd * 4; }
+constexpr int lds_bytes(int hd) {
+    return (lds_k_bytes(hd) + lds_v_bytes(hd) > lds_epilogue_bytes(hd) ? lds_k_bytes(hd) + lds_v_bytes(hd)
+                                                                       : lds_epilogue_bytes(hd)) +
+           kLdsMiscBytes;
+}
+// Shipped geometry: 32 KiB + 16 B (64), 64 KiB + 16 B (128), 128 KiB + 16 B (256)
+constexpr int kCuLdsBytes = 160 * 1024;  // LDS of one gfx950 compute unit
+
+// Head dimensions built: the pages' model uses 128 throughout; 64 and 256
+// are the same kernel with narrower or wider rows.  A geometry supports a
+// head dimension when each wave's share of a key tile is a whole number of
+// direct-to-LDS copies (64 lanes x 16 B: 64 / (hd / 8) rows each) and the
+// work-group's LDS fits a compute unit.
+constexpr bool head_dim_supported(int hd) {
+    return (hd == 64 || hd == 128 || hd == 256) && (kKvTile / kWaves) % (64 / (hd / 8)) == 0 &&
+           lds_bytes(hd) <= kCuLdsBytes;
+}
+
+// Resident work-groups per CU: two (2 waves per SIMD, 256 registers each)
+// for 4-wave groups whose LDS fits twice (head_dim <= 128 with 64-key
+// tiles); otherwise one: head_dim 256's 128 KiB of K/V planes and 8 output
+// blocks per wave need a whole CU's LDS and a SIMD's full register file, and
+// an 8-wave group already puts 2 waves on each SIMD.
+constexpr int groups_per_cu(int hd) { return (kWaves == 4 && 2 * lds_bytes(hd) <= kCuLdsBytes) ? 2 : 1; }
 
 // Work-groups are dispatched round-robin over the 8 XCDs of an MI355X.
 constexpr int kXcds = 8;

@@ -246,6 +246,7 @@ int launch(const void* q, const void* k, const void* v, void* out, int n_q_heads
     const void* fn = head_dim == 64    ? prefill_kernel_hd64(bf16, f32, causal != 0, prio)
                      : head_dim == 128 ? prefill_kernel_hd128(bf16, f32, causal != 0, prio)
                                        : prefill_kernel_hd256(bf16, f32, causal != 0, prio);
+    if (!fn) return fail(FA_ERR_HEAD_DIM, "head_dim %d is not built in this library's tile geometry", head_dim);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)plan.n_groups), dim3(kThreads), args, 0,
                                    static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(FA_ERR_LAUNCH, "hipLaunchKernel: %s", hipGetErrorString(e));

@@ -148,6 +148,8 @@ struct Tile {
     static constexpr int kRowsPerCopy = 64 / kChunks;  // rows per direct-to-LDS instruction
     static constexpr int kCopies = (kKvTile / kWaves) / kRowsPerCopy;  // per wave per tile
     static constexpr int kTileBytes = tile_bytes(HD);
+    // every wave copies whole direct-to-LDS instructions of its share of rows
+    static_assert(kCopies >= 1 && kCopies * kRowsPerCopy * kWaves == kKvTile, "staging covers the tile");
 
     // Chunk permutation of key row r.  Sixteen consecutive rows map one
     // logical chunk to 16 distinct 16-byte bank groups (the K operand reads:
@@ -222,7 +224,7 @@ __device__ __forceinline__ void stage_tile(const char* head_base, uint32_t row_b
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)n_records, kBufferFlags);
 #pragma unroll
     for (int j = 0; j < L::kCopies; ++j) {
-        const int row0 = 16 * wave + L::kRowsPerCopy * j;
+        const int row0 = (kKvTile / kWaves) * wave + L::kRowsPerCopy * j;
         const int row = row0 + lane / L::kChunks;
         const int chunk = (lane % L::kChunks) ^ L::swz(row);
         const uint32_t voff = (uint32_t)row * row_bytes + (uint32_t)chunk * 16u;
@@ -274,10 +276,10 @@ __device__ __forceinline__ typename Operand<T>::x8 load_vt(const char* vtile, co
     return a;
 }
 
-// Scores of one 64-key tile for this wavefront's 32 queries: S^T blocks for
-// keys [0, 32) and [32, 64) of the tile.
+// Scores of one key tile for this wavefront's 32 queries: S^T blocks for
+// keys [32 kb, 32 kb + 32) of the tile, kb < kKb.
 struct TileScores {
-    floatx16 b[2];
+    floatx16 b[kKb];
 };
 
 // Mask the scores of tile t: -inf where the key is past the stored keys or
@@ -290,7 +292,7 @@ __device__ __forceinline__ void mask_scores(TileScores& s, int t, int q_pos, int
     const int last = CAUSAL ? min(q_pos, kv_len - 1) : kv_len - 1;
     const int lim = last - (t * kKvTile + 4 * g);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int off = acc_key(kb, i, 0);
@@ -330,7 +332,7 @@ template <int HD, typename T, bool HAS_CUR, bool HAS_NEXT, bool PREFETCH_V, bool
 __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
                                         const typename Operand<T>::x8 (&qb)[HD / 16],
                                         const TileScores& sc, TileScores& sn,
-                                        typename Operand<T>::x8 (&pb)[4], float& l_part, float m_ref,
+                                        typename Operand<T>::x8 (&pb)[kKs], float& l_part, float m_ref,
                                         float c2, int l32, int g, const char* __restrict__ vtile,
                                         const int (&vt_off)[kVtOffsets<HD>],
                                         typename Operand<T>::x8 (&vf)[4]) {
@@ -338,7 +340,8 @@ __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
     using Op = Operand<T>;
     using X8 = typename Op::x8;
     using X2 = typename Op::x2;
-    constexpr int kSlots = 2 * L::kQFrags;
+    constexpr int kSlots = kKb * L::kQFrags;
+    constexpr int kPairs = 8 * kKb;
     float lsum = 0.0f;
     const int z = L::swz(l32);
     const char* rp = ktile_next + l32 * L::kRowBytes;
@@ -355,7 +358,7 @@ __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
         lsum = Op::sum2(ph, lsum);
     };
     X8 kf[4];
-    floatx16 acc[2] = {};
+    floatx16 acc[kKb] = {};
     if (HAS_NEXT) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) kf[i] = kread(i);
@@ -373,21 +376,21 @@ __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
         if (PREFETCH_V && i >= kSlots - 4) vf[i - (kSlots - 4)] = load_vt_slot<HD, T>(vtile, vt_off, i - (kSlots - 4));
         if (HAS_CUR) {
 #pragma unroll
-            for (int c = i * 16 / kSlots; c < (i + 1) * 16 / kSlots; ++c) valu_chunk(c);
+            for (int c = i * kPairs / kSlots; c < (i + 1) * kPairs / kSlots; ++c) valu_chunk(c);
         }
     }
     if (HAS_CUR && HAS_NEXT) {
         // Register fences: keep the probabilities in this phase (code
         // motion before scheduling would otherwise sink them into phase B).
 #pragma unroll
-        for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[i]));
+        for (int i = 0; i < kKs; ++i) asm volatile("" : "+v"(pb[i]));
         asm volatile("" : "+v"(lsum));
     }
     __builtin_amdgcn_sched_barrier(0);
     if (HAS_CUR && PRIO) __builtin_amdgcn_s_setprio(0);
     if (HAS_NEXT) {
-        sn.b[0] = acc[0];
-        sn.b[1] = acc[1];
+#pragma unroll
+        for (int kb = 0; kb < kKb; ++kb) sn.b[kb] = acc[kb];
     }
     l_part += lsum;
 }
@@ -401,12 +404,13 @@ __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
 // the query), spread over the slots.
 template <int HD, typename T, bool HAS_NEXT>
 __device__ __forceinline__ float phase_b(const char* __restrict__ vtile,
-                                         const typename Operand<T>::x8 (&pb)[4],
+                                         const typename Operand<T>::x8 (&pb)[kKs],
                                          floatx16 (&oacc)[HD / 32], const TileScores& sn, float c2,
                                          int l32, int g, const int (&vt_off)[kVtOffsets<HD>],
                                          typename Operand<T>::x8 (&vf)[4]) {
     using L = Tile<HD>;
-    constexpr int kSlots = 4 * L::kDBlocks;
+    constexpr int kSlots = kKs * L::kDBlocks;
+    constexpr int kPairs = 8 * kKb;
     float mx = -INFINITY;
 #pragma unroll
     for (int f = 0; f < kSlots; ++f) {
@@ -415,7 +419,7 @@ __device__ __forceinline__ float phase_b(const char* __restrict__ vtile,
         if (f + 4 < kSlots) vf[f & 3] = load_vt_slot<HD, T>(vtile, vt_off, f + 4);
         if (HAS_NEXT) {
 #pragma unroll
-            for (int c = f * 16 / kSlots; c < (f + 1) * 16 / kSlots; ++c) {
+            for (int c = f * kPairs / kSlots; c < (f + 1) * kPairs / kSlots; ++c) {
                 const int kb = c >> 3, i = 2 * (c & 7);
                 mx = fmaxf(fmaxf(mx, sn.b[kb][i]), sn.b[kb][i + 1]);
             }
@@ -594,7 +598,7 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
 #pragma unroll
     for (int db = 0; db < ND; ++db) oacc[db] = floatx16{};
     float m_ref = -INFINITY, l_part = 0.0f;
-    X8 pb[4];
+    X8 pb[kKs];
     TileScores sa, sb;
 
     // Prologue: scores and reference maximum of tile 0.
@@ -605,9 +609,16 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
         phase_a<HD, TI, false, true, false, PRIO>(kbuf(0), qb, sa, sa, pb, l_part, m_ref, c2, l32, g, nullptr,
                                             vt_off, vf_unused);
         if (tile_needs_mask<CAUSAL>(t_lo, pos_w, kv_len)) mask_scores<CAUSAL>(sa, t_lo, q_pos, kv_len, g);
-        float mx = fmaxf(sa.b[0][0], sa.b[1][0]);
+        // register i's maximum over the kKb blocks, then over the 16 registers
+        auto block_max = [&](int i) {
+            float m = sa.b[0][i];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sa.b[0][i], sa.b[1][i]));
+            for (int kb = 1; kb < kKb; ++kb) m = fmaxf(m, sa.b[kb][i]);
+            return m;
+        };
+        float mx = block_max(0);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, block_max(i));
         mx = pair_max(mx);
         maybe_rescale<ND>((mx == -INFINITY) ? -INFINITY : mx * c2, m_ref, l_part, oacc);
     }
@@ -804,10 +815,15 @@ const void* pick_kernel_t(bool causal, bool prio) {
 
 template <int HD>
 const void* pick_kernel(bool in_bf16, bool out_f32, bool causal, bool prio) {
-    if (in_bf16)
-        return out_f32 ? pick_kernel_t<HD, __bf16, float>(causal, prio) : pick_kernel_t<HD, __bf16, __bf16>(causal, prio);
-    return out_f32 ? pick_kernel_t<HD, _Float16, float>(causal, prio)
-                   : pick_kernel_t<HD, _Float16, _Float16>(causal, prio);
+    if constexpr (!head_dim_supported(HD)) {
+        return nullptr;  // not built in this geometry
+    } else {
+        if (in_bf16)
+            return out_f32 ? pick_kernel_t<HD, __bf16, float>(causal, prio)
+                           : pick_kernel_t<HD, __bf16, __bf16>(causal, prio);
+        return out_f32 ? pick_kernel_t<HD, _Float16, float>(causal, prio)
+                       : pick_kernel_t<HD, _Float16, _Float16>(causal, prio);
+    }
 }
 
 }  // namespace

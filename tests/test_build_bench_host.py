@@ -94,3 +94,14 @@ def test_noalloc_scratch_covers_every_split_plan():
                 worst = max(worst, p.workspace_bytes)
                 assert p.workspace_bytes <= scratch, (hd, nq, nkv, q_len, kv_len, p.workspace_bytes)
     assert worst > 16 << 20  # the sweep reaches the large splits
+
+
+def test_shipped_geometry_and_other_builds_go_elsewhere():
+    """The library ships 64-key tiles and 4 waves per work-group; builds of
+    other geometries (for measurement) never replace it."""
+    p = fa.fa_prefill_plan(32, 32, 2659, 128, 1)
+    assert (p.kv_tile, p.waves_per_group, p.q_tile) == (64, 4, 128)
+    assert build.SHIPPED_GEOMETRY == (64, 4)
+    other = build.geometry_lib_path(32, 4)
+    assert other != build.LIB_PATH and os.path.basename(other) == build.LIB_NAME
+    assert "kv32_w4" in other
