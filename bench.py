@@ -87,7 +87,7 @@ def cpu_baseline(wl, q, k, v, gpu_out, scale, budget_s: float = 12.0) -> dict:
     except Exception:  # threadpoolctl absent: report the affinity set
         threads = len(os.sched_getaffinity(0))
     group = wl.n_q_heads // wl.n_kv_heads
-    heads, t_used, worst = 0, 0.0, 0.0
+    heads, t_used, worst, worst_rel = 0, 0.0, 0.0, 0.0
     gpu_np = gpu_out.float().cpu().numpy()
     while heads < wl.n_q_heads and t_used < budget_s:
         h = heads
@@ -96,7 +96,9 @@ def cpu_baseline(wl, q, k, v, gpu_out, scale, budget_s: float = 12.0) -> dict:
         oracle_fn = attention_chunk_f64 if wl.chunked else attention_f64
         ref = oracle_fn(q[:, h:h + 1], k[:, hk:hk + 1], v[:, hk:hk + 1], scale, wl.causal)
         t_used += time.perf_counter() - t0
-        worst = max(worst, parity_errors(gpu_np[:, h:h + 1], ref)["max_abs"])
+        err = parity_errors(gpu_np[:, h:h + 1], ref)
+        worst = max(worst, err["max_abs"])
+        worst_rel = max(worst_rel, err["rel_plain_max"])
         heads += 1
     flop = 4 * wl.head_dim * heads * wl.visible_pairs
     return {
@@ -109,6 +111,7 @@ def cpu_baseline(wl, q, k, v, gpu_out, scale, budget_s: float = 12.0) -> dict:
                   f"dense score matrix then mask",
         "seconds": round(t_used, 3),
         "gpu_vs_oracle_max_abs_on_sample": worst,
+        "gpu_vs_oracle_plain_rel_on_sample": worst_rel,  # |g-o|/|o| over |o| >= 0.05
         "host_cpus": len(os.sched_getaffinity(0)),
     }
 

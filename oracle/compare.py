@@ -9,6 +9,10 @@ to |o| ~ 0.03 with occasional |o| ~ 0), while the rounding error of the f16
 probabilities scales with |v|, not |o|.  The relative error is therefore
 taken against max(|o|, REL_FLOOR) with REL_FLOOR = ATOL / RTOL = 0.2, where
 the two criteria coincide; above the floor it is the plain relative error.
+Below the floor the floored figure is max_abs / 0.2, so it adds nothing to
+max_abs there; parity_errors therefore also reports, for information (not
+part of the bar), the plain relative error |g - o| / |o| over the elements
+with |o| >= REL_REPORT_MIN (its maximum and 99.9th percentile).
 """
 
 from __future__ import annotations
@@ -18,6 +22,7 @@ import numpy as np
 ATOL = 2e-3
 RTOL = 1e-2
 REL_FLOOR = ATOL / RTOL  # 0.2
+REL_REPORT_MIN = 0.05    # |o| threshold of the reported plain relative error
 
 # Other element types, derived from the f16 bar:
 # * bf16 inputs: the probabilities enter P.V rounded to bf16, whose unit
@@ -48,14 +53,22 @@ def parity_errors(got, ref, out_unit: float = 0.0) -> dict:
     if g.shape != r.shape:
         raise ValueError(f"shape mismatch {g.shape} vs {r.shape}")
     if g.size == 0:
-        return {"max_abs": 0.0, "max_rel": 0.0, "normwise": 0.0, "finite": True}
+        return {"max_abs": 0.0, "max_rel": 0.0, "normwise": 0.0, "finite": True, "rel_plain_max": 0.0,
+                "rel_plain_p999": 0.0, "rel_plain_count": 0}
     finite = bool(np.all(np.isfinite(g)))
     d = np.maximum(np.abs(g - r) - out_unit * np.abs(r), 0.0)
     max_abs = float(np.max(d)) if finite else float("inf")
     max_rel = float(np.max(d / np.maximum(np.abs(r), REL_FLOOR))) if finite else float("inf")
     denom = float(np.max(np.abs(r)))
     normwise = max_abs / denom if denom > 0 else max_abs
-    return {"max_abs": max_abs, "max_rel": max_rel, "normwise": normwise, "finite": finite}
+    big = np.abs(r) >= REL_REPORT_MIN
+    if finite and np.any(big):
+        rel = d[big] / np.abs(r[big])
+        rel_max, rel_p999 = float(np.max(rel)), float(np.quantile(rel, 0.999))
+    else:
+        rel_max = rel_p999 = float("inf") if not finite else 0.0
+    return {"max_abs": max_abs, "max_rel": max_rel, "normwise": normwise, "finite": finite,
+            "rel_plain_max": rel_max, "rel_plain_p999": rel_p999, "rel_plain_count": int(np.count_nonzero(big))}
 
 
 def within_tolerance(errors: dict, atol: float = ATOL, rtol: float = RTOL) -> bool:

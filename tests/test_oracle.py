@@ -344,6 +344,12 @@ def test_parity_metric():
     assert not within_tolerance(e)
     assert within_tolerance(parity_errors(ref + 1e-3, ref))
     assert not within_tolerance(parity_errors(np.array([np.nan, 0, 0, 0]), ref))
+    # reported plain relative error: over |o| >= 0.05 only (0.1, 1.0, -3.0 here)
+    assert e["rel_plain_count"] == 3
+    assert math.isclose(e["rel_plain_max"], 1e-2)  # 1e-3 / 0.1
+    g = ref + np.array([1.0, 0.0, 0.0, 3e-3])
+    e2 = parity_errors(g, ref)
+    assert math.isclose(e2["rel_plain_max"], 1e-3)  # the error at |o| = 0 is not in the plain figure
 
 
 def test_parity_metric_out_unit_and_bars():

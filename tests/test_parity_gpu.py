@@ -37,7 +37,8 @@ def _run(fa, q, k, v, scale=SCALE, causal=True):
 
 def _report(tag, err):
     print(f"[parity] {tag}: max_abs={err['max_abs']:.3e} max_rel={err['max_rel']:.3e} "
-          f"normwise={err['normwise']:.3e}", flush=True)
+          f"normwise={err['normwise']:.3e} plain_rel(|o|>=0.05) max={err['rel_plain_max']:.3e} "
+          f"p99.9={err['rel_plain_p999']:.3e} over {err['rel_plain_count']}", flush=True)
 
 
 @pytest.mark.parametrize("key", ["tiny", "7b_2k", "7b_2659", "gqa_4k"])
