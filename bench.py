@@ -5,9 +5,12 @@
 
 One step = one fa_prefill launch over the whole workload (32 heads x 2659
 tokens x head_dim 128, causal, f16 in, f32 out by default), inputs resident in
-HBM.  W untimed steps, then K steps back to back on one stream, bracketed by
-device synchronisation and split into B bursts (default 7 x 50) with a HIP
-event on the launch stream at every burst boundary.  The time per step is the
+HBM.  W untimed steps (default 300: after idle the device's power management
+runs a transient, launches first fast, then up to ~30 % slower, settling
+after about 300 launches of this size), then K steps back to back on one
+stream, bracketed by device synchronisation and split into B bursts
+(default 7 x 50) with a HIP event on the launch stream at every burst
+boundary.  The time per step is the
 median burst's time per launch (p10 / p90 / mean over bursts are reported
 too, so the clock's sag under sustained load shows), warm L2 / MALL.  A cold
 figure follows: launches each preceded by a 1 GiB scrub that evicts the
@@ -299,7 +302,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=350, help="timed launches (split into --bursts)")
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed launches first; after idle the device's power management boosts, then "
+                         "dips (launches up to ~30 %% slower) and settles within about 300 launches")
     ap.add_argument("--bursts", type=int, default=7, help="bursts the timed launches are split into")
     ap.add_argument("--cold", type=int, default=10, metavar="N",
                     help="cold-cache launches after the warm bursts (0: skip)")
@@ -440,7 +445,8 @@ def attention_bench(args, key) -> int:
         "timing": {
             "protocol": f"{len(t['burst_sizes'])} bursts of {t['burst_sizes'][0]} back-to-back launches after "
                         f"{args.warmup} warm-up launches, HIP events on the launch stream; ms_per_step = "
-                        f"median burst (warm L2/MALL)",
+                        f"median burst (warm L2/MALL; the power-management transient after idle settles "
+                        f"within about 300 launches)",
             "burst_ms_per_launch": [round(x, 5) for x in t["burst_ms_per_launch"]],
             "ms_p10": round(t["p10"], 5),
             "ms_p90": round(t["p90"], 5),

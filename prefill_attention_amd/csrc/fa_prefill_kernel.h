@@ -45,11 +45,17 @@
 //    key-major V tile with ds_read_b64_tr_b16, whose 16-lane transpose turns
 //    four 8-byte row pieces into four keys of one head-dim column per lane.
 //
-//  * Softmax in base 2: p = 2^(s*scale*log2(e) - m).  The running reference
-//    m is only raised when a tile's maximum exceeds it by more than 8 (log2
-//    units), so p <= 256 stays far inside the 16-bit range; otherwise O and
-//    l are not rescaled at all.  O/l is unchanged in exact arithmetic by the
-//    choice of reference, so the result is the same softmax.
+//  * Softmax in base 2: p = 2^(s*scale*log2(e) - m) against a reference m
+//    set from the first key tile's row maximum.  For head_dim <= 128 no row
+//    maximum is taken afterwards: each lane already sums its rounded
+//    probabilities of a tile for the row sum, and a lane sum <= 2^15 proves
+//    every probability of the lane representable in the 16-bit operand type.
+//    Only when some lane's sum exceeds that does the wavefront raise m to the
+//    tile's row maximum, rescale O and l by 2^(m_old - m_new) and recompute
+//    the tile's probabilities.  Head_dim 256 takes each tile's row maximum
+//    and raises m only when it exceeds m by more than 8 (log2 units), so
+//    p <= 256.  O/l is unchanged in exact arithmetic by the choice of
+//    reference, so the result is the same softmax.
 //
 //  * The validity predicate is "key <= the query's position (causal) and
 //    key < kv_len", both bounds always applied (the pages' tail-tile
@@ -87,8 +93,6 @@ typedef unsigned uintx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
-// Lazy-rescale threshold in log2 units: probabilities stay <= 2^8.
-constexpr float kTau = 8.0f;
 // Buffer descriptor word 3 for raw (untyped) dword access on CDNA.
 constexpr int kBufferFlags = 0x00020000;
 
@@ -324,7 +328,8 @@ __device__ __forceinline__ typename Operand<T>::x8 load_vt_slot(const char* vtil
 //     right after;
 //   VALU (when HAS_CUR): the slot's share of the 16 probability pairs of the
 //     current tile, p = 2^(s*c2 - m) rounded to the operand type into the B
-//     operands of O^T += V^T P^T, and their contribution to the row sum.
+//     operands of O^T += V^T P^T, and their sum over the lane (l_tile, the
+//     lane's share of the tile's row sum).
 // With PREFETCH_V the last four slots also read phase B's first four V^T
 // fragments.  Hard scheduling barriers between slots keep every K read four
 // MFMAs ahead of its use and the exponentials spread under the MFMAs.
@@ -332,7 +337,7 @@ template <int HD, typename T, bool HAS_CUR, bool HAS_NEXT, bool PREFETCH_V, bool
 __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
                                         const typename Operand<T>::x8 (&qb)[HD / 16],
                                         const TileScores& sc, TileScores& sn,
-                                        typename Operand<T>::x8 (&pb)[kKs], float& l_part, float m_ref,
+                                        typename Operand<T>::x8 (&pb)[kKs], float& l_tile, float m_ref,
                                         float c2, int l32, int g, const char* __restrict__ vtile,
                                         const int (&vt_off)[kVtOffsets<HD>],
                                         typename Operand<T>::x8 (&vf)[4]) {
@@ -392,21 +397,33 @@ __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
 #pragma unroll
         for (int kb = 0; kb < kKb; ++kb) sn.b[kb] = acc[kb];
     }
-    l_part += lsum;
+    l_tile = lsum;
 }
 
-// Phase B, as 4 * kDBlocks explicit issue slots (16 for head_dim 128).  Slot
-// f (ks = f / kDBlocks, db = f % kDBlocks): MFMA O^T block db += V^T
+// How the softmax reference follows the scores, per head dimension: with
+// the overflow check (head_dim <= 128) no row maximum is taken after the
+// first tile; head_dim 256, whose one wave per SIMD holds its output in
+// AGPRs, keeps the per-tile row maximum and the rescale threshold kTau
+// instead (the check's recompute path cost it 5 % there).
+template <int HD>
+constexpr bool kOverflowCheck = HD <= 128;
+
+// Rescale threshold of the row-maximum path, in log2 units: probabilities
+// stay <= 2^8.
+constexpr float kTau = 8.0f;
+
+// Phase B, as kKs * kDBlocks explicit issue slots (16 for head_dim 128).
+// Slot f (ks = f / kDBlocks, db = f % kDBlocks): MFMA O^T block db += V^T
 // fragment (db, ks) x P^T fragment ks, the V^T fragment (two transposed LDS
 // reads) having been read four slots earlier (the first four in phase A),
-// then the read for slot f + 4.  VALU (when HAS_NEXT): the next tile's row
-// maximum, returned in log2 units (-inf if the tile has no visible key for
-// the query), spread over the slots.
-template <int HD, typename T, bool HAS_NEXT>
+// then the read for slot f + 4.  VALU (when WANT_MAX, the row-maximum path):
+// the next tile's row maximum, returned in log2 units (-inf if the tile has
+// no visible key for the query), spread over the slots.
+template <int HD, typename T, bool WANT_MAX>
 __device__ __forceinline__ float phase_b(const char* __restrict__ vtile,
                                          const typename Operand<T>::x8 (&pb)[kKs],
                                          floatx16 (&oacc)[HD / 32], const TileScores& sn, float c2,
-                                         int l32, int g, const int (&vt_off)[kVtOffsets<HD>],
+                                         const int (&vt_off)[kVtOffsets<HD>],
                                          typename Operand<T>::x8 (&vf)[4]) {
     using L = Tile<HD>;
     constexpr int kSlots = kKs * L::kDBlocks;
@@ -417,7 +434,7 @@ __device__ __forceinline__ float phase_b(const char* __restrict__ vtile,
         __builtin_amdgcn_sched_barrier(0);
         oacc[f % L::kDBlocks] = Operand<T>::mfma(vf[f & 3], pb[f / L::kDBlocks], oacc[f % L::kDBlocks]);
         if (f + 4 < kSlots) vf[f & 3] = load_vt_slot<HD, T>(vtile, vt_off, f + 4);
-        if (HAS_NEXT) {
+        if (WANT_MAX) {
 #pragma unroll
             for (int c = f * kPairs / kSlots; c < (f + 1) * kPairs / kSlots; ++c) {
                 const int kb = c >> 3, i = 2 * (c & 7);
@@ -427,15 +444,16 @@ __device__ __forceinline__ float phase_b(const char* __restrict__ vtile,
     }
     __builtin_amdgcn_sched_barrier(0);
     float mt = -INFINITY;
-    if (HAS_NEXT) {
+    if (WANT_MAX) {
         mx = pair_max(mx);
         mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
     }
     return mt;
 }
 
-// Raise the softmax reference when some query's tile maximum outgrew it by
-// more than tau; O and l are rescaled by 2^(m_old - m_new) in that case only.
+// Row-maximum path: raise the softmax reference when some query's tile
+// maximum outgrew it by more than kTau; O and l are rescaled by
+// 2^(m_old - m_new) in that case only.
 template <int ND>
 __device__ __forceinline__ void maybe_rescale(float mt, float& m_ref, float& l_part, floatx16 (&oacc)[ND]) {
     if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau)) {
@@ -451,6 +469,54 @@ __device__ __forceinline__ void maybe_rescale(float mt, float& m_ref, float& l_p
         for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
         m_ref = m_new;
     }
+}
+
+// Largest lane sum of one tile's rounded probabilities that proves each of
+// them (all >= 0) representable in f16 (largest finite 65504): p <= 2^15.
+constexpr float kSumLimit = 32768.0f;
+
+// A lane's probabilities of the tile with scores sc summed above kSumLimit
+// (or to inf / NaN): raise the reference to the tile's row maximum (log2
+// units; unchanged for a query with no visible key in the tile), rescale O
+// and l by 2^(m_old - m_new), and recompute the tile's probabilities and
+// lane sum.  Rare: after the first tile only a query whose scores keep
+// growing by more than about 10 (log2 units) triggers it.
+template <int ND, typename T>
+__device__ __forceinline__ void redo_tile(const TileScores& sc, float c2, float& m_ref, float& l_part,
+                                          float& l_tile, floatx16 (&oacc)[ND],
+                                          typename Operand<T>::x8 (&pb)[kKs]) {
+    using Op = Operand<T>;
+    using X2 = typename Op::x2;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc.b[kb][i]);
+    mx = pair_max(mx);
+    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
+    const float m_new = fmaxf(m_ref, mt);
+    // A side effect keeps this rarely taken block from being speculated into
+    // every step; the multiplies stay ordinary code, which gets the
+    // MFMA-to-VALU wait states on the accumulators it reads.
+    asm volatile("" ::: "memory");
+    const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    l_part *= alpha;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
+    m_ref = m_new;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8 * kKb; ++c) {
+        const int kb = c >> 3, e = 2 * (c & 7);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc.b[kb][e], c2, -m_ref));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc.b[kb][e + 1], c2, -m_ref));
+        const floatx2 pf = {p0, p1};
+        const X2 ph = __builtin_convertvector(pf, X2);
+        pb[2 * kb + (e >> 3)][e & 7] = ph[0];
+        pb[2 * kb + (e >> 3)][(e & 7) + 1] = ph[1];
+        lsum = Op::sum2(ph, lsum);
+    }
+    l_tile = lsum;
 }
 
 // Workspace of split launches (laid out by the host for its capacity):
@@ -606,7 +672,8 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     __syncthreads();
     {
         X8 vf_unused[4];
-        phase_a<HD, TI, false, true, false, PRIO>(kbuf(0), qb, sa, sa, pb, l_part, m_ref, c2, l32, g, nullptr,
+        float l_unused = 0.0f;
+        phase_a<HD, TI, false, true, false, PRIO>(kbuf(0), qb, sa, sa, pb, l_unused, m_ref, c2, l32, g, nullptr,
                                             vt_off, vf_unused);
         if (tile_needs_mask<CAUSAL>(t_lo, pos_w, kv_len)) mask_scores<CAUSAL>(sa, t_lo, q_pos, kv_len, g);
         // register i's maximum over the kKb blocks, then over the 16 registers
@@ -620,33 +687,51 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
 #pragma unroll
         for (int i = 1; i < 16; ++i) mx = fmaxf(mx, block_max(i));
         mx = pair_max(mx);
-        maybe_rescale<ND>((mx == -INFINITY) ? -INFINITY : mx * c2, m_ref, l_part, oacc);
+        // Every query sees a key in its first tile (tile 0, or a split
+        // part's first tile, which starts at or before the query tile's
+        // first position), so the reference is finite from here on.
+        m_ref = (mx == -INFINITY) ? -INFINITY : mx * c2;
     }
 
     // Pipeline step for tile j (its scores in sc), producing the scores of
-    // tile j + 1 in sn.  On entry K(j+1) and V(j) have been issued; the
-    // barrier also frees kbuf(j) and vbuf(j - 1) for K(j+2) and V(j+1).
+    // tile j + 1 in sn; with the overflow check the tile's probabilities are
+    // checked against kSumLimit before P.V uses them, otherwise phase B also
+    // takes tile j + 1's row maximum for the rescale test.  On entry K(j+1) and V(j) have been
+    // issued; the barrier also frees kbuf(j) and vbuf(j - 1) for K(j+2) and
+    // V(j+1).
     auto step = [&](int j, TileScores& sc, TileScores& sn) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (j + 2 < n_tiles) stage_tile<HD>(k_head, kv_row_bytes, hk, kv_len, kv_row(j + 2), kbuf(j + 2), wave, lane);
         stage_tile<HD>(v_head, kv_row_bytes, hk, kv_len, kv_row(j + 1), vbuf(j + 1), wave, lane);
         X8 vf[4];
-        phase_a<HD, TI, true, true, true, PRIO>(kbuf(j + 1), qb, sc, sn, pb, l_part, m_ref, c2, l32, g, vbuf(j),
+        float l_tile;
+        phase_a<HD, TI, true, true, true, PRIO>(kbuf(j + 1), qb, sc, sn, pb, l_tile, m_ref, c2, l32, g, vbuf(j),
                                           vt_off, vf);
+        if constexpr (kOverflowCheck<HD>) {
+            if (__builtin_amdgcn_ballot_w64(!(l_tile <= kSumLimit)))
+                redo_tile<ND, TI>(sc, c2, m_ref, l_part, l_tile, oacc, pb);
+        }
+        l_part += l_tile;
         if (tile_needs_mask<CAUSAL>(t_lo + j + 1, pos_w, kv_len))
             mask_scores<CAUSAL>(sn, t_lo + j + 1, q_pos, kv_len, g);
-        const float mt = phase_b<HD, TI, true>(vbuf(j), pb, oacc, sn, c2, l32, g, vt_off, vf);
-        maybe_rescale<ND>(mt, m_ref, l_part, oacc);
+        const float mt = phase_b<HD, TI, !kOverflowCheck<HD>>(vbuf(j), pb, oacc, sn, c2, vt_off, vf);
+        if constexpr (!kOverflowCheck<HD>) maybe_rescale<ND>(mt, m_ref, l_part, oacc);
     };
     // Last tile: probabilities and P.V only.
     auto last = [&](int j, TileScores& sc) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         X8 vf[4];
-        phase_a<HD, TI, true, false, true, PRIO>(nullptr, qb, sc, sc, pb, l_part, m_ref, c2, l32, g, vbuf(j),
+        float l_tile;
+        phase_a<HD, TI, true, false, true, PRIO>(nullptr, qb, sc, sc, pb, l_tile, m_ref, c2, l32, g, vbuf(j),
                                            vt_off, vf);
-        phase_b<HD, TI, false>(vbuf(j), pb, oacc, sc, c2, l32, g, vt_off, vf);
+        if constexpr (kOverflowCheck<HD>) {
+            if (__builtin_amdgcn_ballot_w64(!(l_tile <= kSumLimit)))
+                redo_tile<ND, TI>(sc, c2, m_ref, l_part, l_tile, oacc, pb);
+        }
+        l_part += l_tile;
+        phase_b<HD, TI, false>(vbuf(j), pb, oacc, sc, c2, vt_off, vf);
     };
 
     // One copy of the last tile's code: with an even tile count the odd step

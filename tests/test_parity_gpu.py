@@ -106,11 +106,52 @@ def test_tail_sweep_causal(fa, S, heads):
 @pytest.mark.parametrize("S", [300, 700, 1024, 1500])
 def test_peaked_rows_rescale(fa, S):
     """K x 3 makes the row maximum grow mid-sequence, so the running softmax
-    reference is raised and O rescaled on many tiles (the rescale multiplies
+    reference is raised and O rescaled on some tiles (the rescale multiplies
     read MFMA results; a missing MFMA-to-VALU wait shows up here)."""
     q, k, v = make_custom_inputs(S, 4, 1, seed=4000 + S, k_mult=3.0)
     err = parity_errors(_run(fa, q, k, v), attention_f64(q, k, v, SCALE, True))
     assert within_tolerance(err), (S, err)
+
+
+def _growing_keys(S, n_q, n_kv, seed, step_log2=16.3, jump_at=None):
+    """Queries along one direction u and keys along u with a magnitude that
+    grows with the position, so that every 64-key tile's scores exceed the
+    previous tile's by about step_log2 (log2 units) and the kernel's
+    probability sums overflow its limit on every tile; with jump_at, keys
+    from that position on jump by far more (the first exponentials become
+    inf).  Small seeded noise keeps rows and heads distinct."""
+    q, k, v = make_custom_inputs(S, n_q, n_kv, seed=seed)
+    u = torch.full((128,), 0.5)
+    per_key = step_log2 / 64 / (SCALE * 32.0 * 1.4426950408889634)  # |u|^2 = 32
+    t = 1.0 + per_key * torch.arange(S, dtype=torch.float32)
+    if jump_at is not None:
+        t[jump_at:] += 40.0
+    q = (u + 0.05 * q.float()).half()
+    k = (t[:, None, None] * u + 0.05 * k.float()).half()
+    return q, k, v
+
+
+@pytest.mark.parametrize("S,jump", [(700, None), (1500, None), (700, 650), (300, 100)])
+def test_reference_raised_on_every_tile(fa, S, jump):
+    """Scores that keep growing from tile to tile (and a sudden jump of ~180
+    in log2 units): the probabilities of a tile overflow the sum limit and
+    are recomputed against a raised reference, with O and l rescaled."""
+    q, k, v = _growing_keys(S, 4, 2, seed=4100 + S, jump_at=jump)
+    err = parity_errors(_run(fa, q, k, v), attention_f64(q, k, v, SCALE, True))
+    _report(f"growing keys S={S} jump={jump}", err)
+    assert within_tolerance(err), (S, jump, err)
+
+
+def test_reference_raised_in_split_parts(fa):
+    """The same growing keys under a split chunk: every part raises its own
+    reference, and the merge weighs the parts by m + log2(l)."""
+    q, k, v = _growing_keys(4096, 8, 2, seed=4200)
+    q = q[-3:].contiguous()
+    assert fa.fa_prefill_chunk_plan(8, 2, 3, 4096, 128, 1).kv_splits > 1
+    got = _run_chunk(fa, q, k, v)
+    err = parity_errors(got, attention_chunk_f64(q, k, v, SCALE, True))
+    _report("growing keys, split chunk 3 over 4096", err)
+    assert within_tolerance(err), err
 
 
 @pytest.mark.parametrize("S", [1, 17, 64, 65, 200, 256])
