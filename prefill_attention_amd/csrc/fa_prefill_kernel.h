@@ -131,15 +131,20 @@ struct Operand<__bf16> {
 };
 
 // Four consecutive outputs of a row, converted to the output type (round to
-// nearest even) and stored with one vector store.
-__device__ __forceinline__ void store4(float* p, floatx4 o) { *reinterpret_cast<floatx4*>(p) = o; }
+// nearest even) and stored with one non-temporal vector store: the output is
+// written once and not read again by the kernel, so it is not kept in the L2
+// (measured 1-2.6 % faster up to 4k tokens, where the f32 output is a large
+// share of the launch's traffic, than ordinary stores).
+__device__ __forceinline__ void store4(float* p, floatx4 o) {
+    __builtin_nontemporal_store(o, reinterpret_cast<floatx4*>(p));
+}
 __device__ __forceinline__ void store4(_Float16* p, floatx4 o) {
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    *reinterpret_cast<h4*>(p) = __builtin_convertvector(o, h4);
+    __builtin_nontemporal_store(__builtin_convertvector(o, h4), reinterpret_cast<h4*>(p));
 }
 __device__ __forceinline__ void store4(__bf16* p, floatx4 o) {
     typedef __bf16 b4 __attribute__((ext_vector_type(4)));
-    *reinterpret_cast<b4*>(p) = __builtin_convertvector(o, b4);
+    __builtin_nontemporal_store(__builtin_convertvector(o, b4), reinterpret_cast<b4*>(p));
 }
 
 // Per-head-dimension layout of a K/V tile in LDS.
