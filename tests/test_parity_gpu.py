@@ -142,6 +142,30 @@ def test_reference_raised_on_every_tile(fa, S, jump):
     assert within_tolerance(err), (S, jump, err)
 
 
+@pytest.mark.parametrize("hd,in_dtype,causal", [(64, "f16", True), (128, "bf16", True), (128, "f16", False),
+                                                 (256, "f16", True)])
+def test_reference_raised_other_variants(fa, hd, in_dtype, causal):
+    """Growing keys through the other variants: head_dim 64 and bf16 inputs
+    use the overflow check, head_dim 256 the per-tile row maximum; full
+    (non-causal) attention sees the largest keys from the first tile on."""
+    from oracle import OUT_UNIT, bar
+
+    S = 600
+    q, k, v = make_custom_inputs(S, 4, 2, seed=4300 + hd, head_dim=hd, in_dtype=in_dtype)
+    tt = torch.bfloat16 if in_dtype == "bf16" else torch.float16
+    u = torch.full((hd,), 0.5)
+    scale = float(np.float32(1.0 / np.sqrt(hd)))
+    per_key = 16.3 / 64 / (scale * 0.25 * hd * 1.4426950408889634)
+    t = 1.0 + per_key * torch.arange(S, dtype=torch.float32)
+    q = (u + 0.05 * q.float()).to(tt)
+    k = (t[:, None, None] * u + 0.05 * k.float()).to(tt)
+    out = fa.attention(q.cuda(), k.cuda(), v.cuda(), scale, causal)
+    torch.cuda.synchronize()
+    err = parity_errors(out.cpu().numpy().astype(np.float64), attention_f64(q, k, v, scale, causal), OUT_UNIT["f32"])
+    _report(f"growing keys hd={hd} {in_dtype} causal={causal}", err)
+    assert within_tolerance(err, *bar(in_dtype)), err
+
+
 def test_reference_raised_in_split_parts(fa):
     """The same growing keys under a split chunk: every part raises its own
     reference, and the merge weighs the parts by m + log2(l)."""
