@@ -133,7 +133,7 @@ typedef struct fa_plan {
                                 not a multiple of 8 (padding work-groups exit at once) */
     int stages;              /* K/V tiles resident in LDS                          */
     int lds_bytes;           /* LDS per work-group: the sum of its planes (K, V and
-                                a 16-byte flag)                                    */
+                                the query plane)                                   */
     int lds_k_bytes;         /* K planes: stages x [kv_tile][head_dim] 16-bit      */
     int lds_v_bytes;         /* V planes: stages x [kv_tile][head_dim] 16-bit      */
     long long kv_tiles_visited; /* KV tiles the grid visits (causal tiles skipped) */
@@ -143,6 +143,9 @@ typedef struct fa_plan {
                                 half of each tile step (a throughput-bound launch);
                                 0: default arbitration (a launch whose heaviest query
                                 tile sets its length); no effect on the results */
+    int lds_q_bytes;         /* query plane: the 32 query rows ([32][head_dim] 16-bit)
+                                of each wave that does not stage them in the second
+                                V stage (at least 16 bytes: a split launch's flag) */
 } fa_plan;
 
 /*

@@ -57,6 +57,7 @@ class FaPlan(ctypes.Structure):
         ("workspace_bytes", ctypes.c_longlong),
         ("groups_per_cu", ctypes.c_int),
         ("phase_priority", ctypes.c_int),
+        ("lds_q_bytes", ctypes.c_int),
     ]
 
     def as_dict(self) -> dict:

@@ -56,16 +56,27 @@ constexpr int row_bytes(int hd) { return hd * 2; }
 constexpr int tile_bytes(int hd) { return kKvTile * row_bytes(hd); }   // one K or V tile
 constexpr int lds_k_bytes(int hd) { return kStages * tile_bytes(hd); }
 constexpr int lds_v_bytes(int hd) { return kStages * tile_bytes(hd); }
-constexpr int kLdsMiscBytes = 16;                                       // the merge-election flag
+// Query plane.  Each wave copies its 32 query rows into LDS (the K tiles'
+// direct-to-LDS loads and chunk permutation: whole rows per instruction) and
+// reads its Q^T fragments from there once.  The first kQWavesInStage waves
+// use the second V stage, which is free until the first step stages V(1);
+// the others use this plane.  A split launch's merge-election flag reuses the
+// plane after the prologue, so it is at least 16 bytes.
+constexpr int kQWavesInStage = kKvTile / kQRowsPerWave < kWaves ? kKvTile / kQRowsPerWave : kWaves;
+constexpr int kLdsFlagBytes = 16;
+constexpr int lds_q_bytes(int hd) {
+    return (kWaves - kQWavesInStage) * kQRowsPerWave * row_bytes(hd) > kLdsFlagBytes
+               ? (kWaves - kQWavesInStage) * kQRowsPerWave * row_bytes(hd)
+               : kLdsFlagBytes;
+}
 // The epilogue reuses the planes to write each wave's 32 f32 output rows
 // row-major; a work-group needs the larger of the two.
 constexpr int lds_epilogue_bytes(int hd) { return kWaves * kQRowsPerWave * hd * 4; }
+constexpr int lds_planes_bytes(int hd) { return lds_k_bytes(hd) + lds_v_bytes(hd) + lds_q_bytes(hd); }
 constexpr int lds_bytes(int hd) {
-    return (lds_k_bytes(hd) + lds_v_bytes(hd) > lds_epilogue_bytes(hd) ? lds_k_bytes(hd) + lds_v_bytes(hd)
-                                                                       : lds_epilogue_bytes(hd)) +
-           kLdsMiscBytes;
+    return lds_planes_bytes(hd) > lds_epilogue_bytes(hd) ? lds_planes_bytes(hd) : lds_epilogue_bytes(hd);
 }
-// Shipped geometry: 32 KiB + 16 B (64), 64 KiB + 16 B (128), 128 KiB + 16 B (256)
+// Shipped geometry: 40 KiB (head_dim 64), 80 KiB (128), 160 KiB (256)
 constexpr int kCuLdsBytes = 160 * 1024;  // LDS of one gfx950 compute unit
 
 // Head dimensions built: the pages' model uses 128 throughout; 64 and 256
@@ -80,7 +91,7 @@ constexpr bool head_dim_supported(int hd) {
 
 // Resident work-groups per CU: two (2 waves per SIMD, 256 registers each)
 // for 4-wave groups whose LDS fits twice (head_dim <= 128 with 64-key
-// tiles); otherwise one: head_dim 256's 128 KiB of K/V planes and 8 output
+// tiles); otherwise one: head_dim 256's 160 KiB of planes and 8 output
 // blocks per wave need a whole CU's LDS and a SIMD's full register file, and
 // an 8-wave group already puts 2 waves on each SIMD.
 constexpr int groups_per_cu(int hd) { return (kWaves == 4 && 2 * lds_bytes(hd) <= kCuLdsBytes) ? 2 : 1; }

@@ -181,6 +181,7 @@ int make_plan(int n_q_heads, int n_kv_heads, int q_len, int kv_len, int head_dim
         plan->lds_bytes = lds_bytes(head_dim);
         plan->lds_k_bytes = lds_k_bytes(head_dim);
         plan->lds_v_bytes = lds_v_bytes(head_dim);
+        plan->lds_q_bytes = lds_q_bytes(head_dim);
         plan->groups_per_cu = groups_per_cu(head_dim);
         long long tiles = 0, max_tiles = 0;
         for (long long t = 0; t < n_q_tiles; ++t) {

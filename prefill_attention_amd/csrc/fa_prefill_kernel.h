@@ -242,6 +242,34 @@ __device__ __forceinline__ void stage_tile(const char* head_base, uint32_t row_b
     }
 }
 
+// Copy this wavefront's 32 query rows [r0, r0 + 32) of head h into LDS,
+// whole rows per instruction like a K tile (lane i fills physical chunk
+// i % kChunks of its row from logical chunk (i % kChunks) ^ swz(row)), so
+// that the Q^T fragments read back exactly like K fragments.  q_bytes points
+// at q, row_stride is n_q_heads rows of head_dim 16-bit elements.  The buffer
+// record ends at the last query row (none when the wave starts past q_len),
+// so rows >= q_len read as zeros.
+template <int HD>
+__device__ __forceinline__ void stage_q(const char* q_bytes, uint32_t row_stride, int h, int q_len, int r0,
+                                        char* dst, int lane) {
+    using L = Tile<HD>;
+    const char* base = q_bytes + (size_t)(uint32_t)r0 * row_stride + (size_t)h * L::kRowBytes;
+    const int rows_left = q_len - r0;
+    const uint32_t n_records = rows_left >= kQRowsPerWave ? (uint32_t)kQRowsPerWave * row_stride
+                               : rows_left > 0 ? (uint32_t)rows_left * row_stride - (uint32_t)h * L::kRowBytes
+                                               : 0u;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)n_records, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < kQRowsPerWave / L::kRowsPerCopy; ++j) {
+        const int row0 = L::kRowsPerCopy * j;
+        const int row = row0 + lane / L::kChunks;
+        const int chunk = (lane % L::kChunks) ^ L::swz(row);
+        const uint32_t voff = (uint32_t)row * row_stride + (uint32_t)chunk * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + row0 * L::kRowBytes), 16, voff, 0, 0, 0);
+    }
+}
+
 // A operand of O^T += V^T P^T for head-dim block db and key step ks: the
 // 32 x 16 slice V^T[32db .. 32db+31][16ks .. 16ks+15] in the slot order of
 // the probability registers (slot (g, e) <-> key 16ks + 8(e/4) + 4g + e%4).
@@ -644,22 +672,13 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     stage_tile<HD>(v_head, kv_row_bytes, hk, kv_len, kv_row(0), vbuf(0), wave, lane);
     if (n_tiles > 1) stage_tile<HD>(k_head, kv_row_bytes, hk, kv_len, kv_row(1), kbuf(1), wave, lane);
 
-    // Q^T as the B operand: lane (l32, g) holds q[my_q][h][16t + 8g .. +8).
-    // q_mode 1 negates Q (negative scale: a sign-bit flip, exact), 2 zeroes
-    // it (scale 0).
-    X8 qb[L::kQFrags];
-    {
-        const bool in = my_q < q_len && q_mode != 2;
-        const TI* qrow = q + ((size_t)my_q * n_q_heads + h) * HD + 8 * g;
-#pragma unroll
-        for (int t = 0; t < L::kQFrags; ++t)
-            qb[t] = in ? *reinterpret_cast<const X8*>(qrow + 16 * t) : X8{};
-        if (q_mode == 1) {
-#pragma unroll
-            for (int t = 0; t < L::kQFrags; ++t)
-                qb[t] = __builtin_bit_cast(X8, __builtin_bit_cast(uintx4, qb[t]) ^ 0x80008000u);
-        }
-    }
+    // This wave's 32 query rows, staged through LDS (read back after the
+    // first barrier): in the second V stage for the first kQWavesInStage
+    // waves, in the query plane for the others.
+    char* const q_lds = wave < kQWavesInStage ? vbuf(1) + wave * kQRowsPerWave * L::kRowBytes
+                                              : lds + lds_k_bytes(HD) + lds_v_bytes(HD) +
+                                                    (wave - kQWavesInStage) * kQRowsPerWave * L::kRowBytes;
+    stage_q<HD>(reinterpret_cast<const char*>(q), (uint32_t)n_q_heads * L::kRowBytes, h, q_len, qw, q_lds, lane);
 
     int vt_off[kVtOffsets<HD>];
 #pragma unroll
@@ -672,9 +691,29 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     X8 pb[kKs];
     TileScores sa, sb;
 
-    // Prologue: scores and reference maximum of tile 0.
+    // Prologue: Q^T, then the scores and reference maximum of tile 0.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    // Q^T as the B operand: lane (l32, g) holds q[my_q][h][16t + 8g .. +8),
+    // the K fragment pattern of the staged rows.  q_mode 1 negates Q
+    // (negative scale: a sign-bit flip, exact), 2 zeroes it (scale 0).  The
+    // wave reads only rows its own loads wrote; V(1) overwrites the second V
+    // stage only after the next barrier.
+    X8 qb[L::kQFrags];
+    {
+        const char* qr = q_lds + l32 * L::kRowBytes;
+        const int zq = L::swz(l32);
+#pragma unroll
+        for (int t = 0; t < L::kQFrags; ++t) qb[t] = load_k_frag<HD, TI>(qr, zq, g, 0, t);
+        if (q_mode == 2) {
+#pragma unroll
+            for (int t = 0; t < L::kQFrags; ++t) qb[t] = X8{};
+        } else if (q_mode == 1) {
+#pragma unroll
+            for (int t = 0; t < L::kQFrags; ++t)
+                qb[t] = __builtin_bit_cast(X8, __builtin_bit_cast(uintx4, qb[t]) ^ 0x80008000u);
+        }
+    }
     {
         X8 vf_unused[4];
         float l_unused = 0.0f;

@@ -74,8 +74,8 @@ static void plans() {
     expect(fa_prefill_plan(65536, 1, INT_MAX, 128, 0, 0, &p) == FA_ERR_SHAPE, "huge tensor", 0, 0);
     // LDS limits
     expect(fa_prefill_plan(4, 4, 10, 256, 1, 65536, &p) == FA_ERR_RESOURCE, "lds 256", 0, 0);
-    expect(fa_prefill_plan(4, 4, 10, 128, 1, 65552, &p) == FA_OK, "lds 128 fits", 0, 0);
-    expect(fa_prefill_plan(4, 4, 10, 128, 1, 65551, &p) == FA_ERR_RESOURCE, "lds 128 one short", 0, 0);
+    expect(fa_prefill_plan(4, 4, 10, 128, 1, 81920, &p) == FA_OK, "lds 128 fits", 0, 0);
+    expect(fa_prefill_plan(4, 4, 10, 128, 1, 81919, &p) == FA_ERR_RESOURCE, "lds 128 one short", 0, 0);
     // NULL plan pointer: validation only
     expect(fa_prefill_plan(32, 32, 2659, 128, 1, 0, nullptr) == FA_OK, "null plan", 0, 0);
     expect(std::strlen(fa_prefill_last_error()) == 0, "no error after success", 0, 0);

@@ -101,11 +101,16 @@ def test_seq_len_zero_is_ok_without_gpu():
 ])
 def test_plan_geometry(S, nq, nkv, causal, hd):
     p = fa.fa_prefill_plan(nq, nkv, S, hd, causal)
-    # the LDS request is exactly the sum of the planes the kernel lays out
-    # (K and V stages, and a 16-byte merge flag)
-    assert p.lds_bytes == p.lds_k_bytes + p.lds_v_bytes + 16
+    # the LDS request is exactly the sum of the planes the kernel lays out:
+    # K and V stages, and the query rows of the waves that do not fit in the
+    # second V stage (the epilogue's f32 rows reuse the same bytes)
+    assert p.lds_bytes == p.lds_k_bytes + p.lds_v_bytes + p.lds_q_bytes
+    assert p.lds_bytes >= p.waves_per_group * 32 * hd * 4
     assert p.lds_k_bytes == p.stages * p.kv_tile * hd * 2
     assert p.lds_v_bytes == p.stages * p.kv_tile * hd * 2
+    in_stage = min(p.waves_per_group, p.kv_tile // 32)
+    assert p.lds_q_bytes == max((p.waves_per_group - in_stage) * 32 * hd * 2, 16)
+    assert p.lds_bytes == {64: 40, 128: 80, 256: 160}[hd] * 1024
     assert p.groups_per_cu == (1 if hd == 256 else 2)
     assert p.lds_bytes * p.groups_per_cu <= 160 * 1024  # the resident work-groups fit 160 KiB
     assert p.threads_per_group == 64 * p.waves_per_group
