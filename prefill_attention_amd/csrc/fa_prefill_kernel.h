@@ -362,7 +362,12 @@ __device__ __forceinline__ typename Operand<T>::x8 load_vt_slot(const char* vtil
 //   VALU (when HAS_CUR): the slot's share of the 16 probability pairs of the
 //     current tile, p = 2^(s*c2 - m) rounded to the operand type into the B
 //     operands of O^T += V^T P^T, and their sum over the lane (l_tile, the
-//     lane's share of the tile's row sum).
+//     lane's share of the tile's row sum).  Each pair is spread over three
+//     slots -- exponent arguments, exponentials, rounding -- so that the VALU
+//     work issued in one slot has no dependency inside it (bitwise the same
+//     values; 1-3 % faster than doing a pair's three steps in one slot).
+//     Register fences pin each step to its slot: the slot barriers alone do
+//     not stop earlier passes from moving pure VALU between slots.
 // With PREFETCH_V the last four slots also read phase B's first four V^T
 // fragments.  Hard scheduling barriers between slots keep every K read four
 // MFMAs ahead of its use and the exponentials spread under the MFMAs.
@@ -384,22 +389,38 @@ __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
     const int z = L::swz(l32);
     const char* rp = ktile_next + l32 * L::kRowBytes;
     auto kread = [&](int i) { return load_k_frag<HD, T>(rp, z, g, i / L::kQFrags, i % L::kQFrags); };
-    // VALU chunk c: probabilities 2c and 2c + 1 of the current tile.
-    auto valu_chunk = [&](int c) {
+    // Pair c (probabilities 2c, 2c + 1): exponent arguments (FMA) one slot
+    // ahead of its exponentials, rounding and row sum one slot behind.
+    float xa[kPairs][2], pe[kPairs][2];
+    auto pre = [&](int c) {
         const int kb = c >> 3, e = 2 * (c & 7);
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc.b[kb][e], c2, -m_ref));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc.b[kb][e + 1], c2, -m_ref));
-        const floatx2 pf = {p0, p1};
+        xa[c][0] = fmaf(sc.b[kb][e], c2, -m_ref);
+        xa[c][1] = fmaf(sc.b[kb][e + 1], c2, -m_ref);
+        asm volatile("" : "+v"(xa[c][0]), "+v"(xa[c][1]));
+    };
+    auto mid = [&](int c) {
+        pe[c][0] = __builtin_amdgcn_exp2f(xa[c][0]);
+        pe[c][1] = __builtin_amdgcn_exp2f(xa[c][1]);
+        asm volatile("" : "+v"(pe[c][0]), "+v"(pe[c][1]));
+    };
+    auto post = [&](int c) {
+        const int kb = c >> 3, e = 2 * (c & 7);
+        const floatx2 pf = {pe[c][0], pe[c][1]};
         const X2 ph = __builtin_convertvector(pf, X2);
         pb[2 * kb + (e >> 3)][e & 7] = ph[0];
         pb[2 * kb + (e >> 3)][(e & 7) + 1] = ph[1];
         lsum = Op::sum2(ph, lsum);
     };
+    auto c_lo = [&](int i) { return i * kPairs / kSlots; };
     X8 kf[4];
     floatx16 acc[kKb] = {};
     if (HAS_NEXT) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) kf[i] = kread(i);
+    }
+    if (HAS_CUR) {
+#pragma unroll
+        for (int c = c_lo(0); c < c_lo(1); ++c) pre(c);
     }
     // Optional issue priority for the VALU-bound phase (the kernel's PRIO).
     if (HAS_CUR && PRIO) __builtin_amdgcn_s_setprio(1);
@@ -413,9 +434,22 @@ __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
         // The first four V^T fragments of phase B, read while the K reads wind down.
         if (PREFETCH_V && i >= kSlots - 4) vf[i - (kSlots - 4)] = load_vt_slot<HD, T>(vtile, vt_off, i - (kSlots - 4));
         if (HAS_CUR) {
+            if (i > 0) {
 #pragma unroll
-            for (int c = i * kPairs / kSlots; c < (i + 1) * kPairs / kSlots; ++c) valu_chunk(c);
+                for (int c = c_lo(i - 1); c < c_lo(i); ++c) post(c);
+            }
+#pragma unroll
+            for (int c = c_lo(i); c < c_lo(i + 1); ++c) mid(c);
+            if (i + 1 < kSlots) {
+#pragma unroll
+                for (int c = c_lo(i + 1); c < c_lo(i + 2); ++c) pre(c);
+            }
         }
+    }
+    if (HAS_CUR) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = c_lo(kSlots - 1); c < kPairs; ++c) post(c);
     }
     if (HAS_CUR && HAS_NEXT) {
         // Register fences: keep the probabilities in this phase (code
