@@ -140,7 +140,8 @@ typedef struct fa_plan {
     long long workspace_bytes;  /* library-owned device scratch the call needs (0: none) */
     int groups_per_cu;       /* work-groups resident per compute unit (2; 1 for head_dim 256) */
     int phase_priority;      /* 1: wavefronts raise their issue priority in the VALU-bound
-                                half of each tile step (a throughput-bound launch);
+                                half of each tile step and read a step's first key
+                                fragments before issuing its loads (a throughput-bound launch);
                                 0: default arbitration (a launch whose heaviest query
                                 tile sets its length); no effect on the results */
     int lds_q_bytes;         /* query plane: the 32 query rows ([32][head_dim] 16-bit)

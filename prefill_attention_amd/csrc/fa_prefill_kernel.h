@@ -217,18 +217,19 @@ __device__ __forceinline__ typename Operand<T>::x8 load_k_frag(const char* row, 
 // points at row 0 of head hk in src ([kv_len][n_kv][HD], 16-bit).  This
 // wavefront copies rows 16*wave .. 16*wave + 15, 1 KiB per instruction.
 // Lane i of an instruction fills physical chunk i % kChunks of its row, so it
-// loads logical chunk (i % kChunks) ^ swz(row).  The buffer record ends at
-// the last valid row of this head, so rows >= kv_len read as 0; the record
-// size is formed in 32 bits from the rows left (at least one).
+// loads logical chunk (i % kChunks) ^ swz(row).  The buffer record is
+// min(rows left, 64) * row_bytes - hk * (one head's row segment): with fewer
+// than 64 rows left it ends exactly at the tensor's end, so rows >= kv_len
+// read as 0; with 64 or more it still covers the tile's 64 rows of this head,
+// whose last byte lies n_kv - hk - 1 segments before 64 * row_bytes.  Formed
+// in 32 bits (rows left >= 1), without a branch.
 template <int HD>
 __device__ __forceinline__ void stage_tile(const char* head_base, uint32_t row_bytes, int hk, int kv_len,
                                            int kt, char* tile, int wave, int lane) {
     using L = Tile<HD>;
     const char* base = head_base + (uint64_t)(uint32_t)kt * row_bytes;
     const int rows_left = kv_len - kt;
-    const uint32_t n_records = rows_left >= kKvTile
-                                   ? (uint32_t)kKvTile * row_bytes
-                                   : (uint32_t)rows_left * row_bytes - (uint32_t)hk * L::kRowBytes;
+    const uint32_t n_records = (uint32_t)min(rows_left, kKvTile) * row_bytes - (uint32_t)hk * L::kRowBytes;
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)n_records, kBufferFlags);
 #pragma unroll
@@ -313,6 +314,16 @@ __device__ __forceinline__ typename Operand<T>::x8 load_vt(const char* vtile, co
     return a;
 }
 
+// The first four K fragments (slots 0..3 of phase A) of the staged key tile.
+template <int HD, typename T>
+__device__ __forceinline__ void load_k_first(typename Operand<T>::x8 (&kf)[4], const char* ktile, int l32, int g) {
+    using L = Tile<HD>;
+    const char* rp = ktile + l32 * L::kRowBytes;
+    const int z = L::swz(l32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kf[i] = load_k_frag<HD, T>(rp, z, g, i / L::kQFrags, i % L::kQFrags);
+}
+
 // Scores of one key tile for this wavefront's 32 queries: S^T blocks for
 // keys [32 kb, 32 kb + 32) of the tile, kb < kKb.
 struct TileScores {
@@ -357,8 +368,8 @@ __device__ __forceinline__ typename Operand<T>::x8 load_vt_slot(const char* vtil
 // head_dim 128).  Slot i (kb = i / kQFrags, t = i % kQFrags):
 //   MFMA (when HAS_NEXT): S^T block kb of the next tile += K fragment t x Q^T
 //     fragment t; the K fragment was read from LDS four slots earlier into
-//     one of four rotating registers, and the read for slot i + 4 is issued
-//     right after;
+//     one of four rotating registers (the first four by the caller:
+//     kf_first), and the read for slot i + 4 is issued right after;
 //   VALU (when HAS_CUR): the slot's share of the 16 probability pairs of the
 //     current tile, p = 2^(s*c2 - m) rounded to the operand type into the B
 //     operands of O^T += V^T P^T, and their sum over the lane (l_tile, the
@@ -372,7 +383,7 @@ __device__ __forceinline__ typename Operand<T>::x8 load_vt_slot(const char* vtil
 // fragments.  Hard scheduling barriers between slots keep every K read four
 // MFMAs ahead of its use and the exponentials spread under the MFMAs.
 template <int HD, typename T, bool HAS_CUR, bool HAS_NEXT, bool PREFETCH_V, bool PRIO>
-__device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
+__device__ __forceinline__ void phase_a(const typename Operand<T>::x8 (&kf_first)[4], const char* __restrict__ ktile_next,
                                         const typename Operand<T>::x8 (&qb)[HD / 16],
                                         const TileScores& sc, TileScores& sn,
                                         typename Operand<T>::x8 (&pb)[kKs], float& l_tile, float m_ref,
@@ -416,7 +427,7 @@ __device__ __forceinline__ void phase_a(const char* __restrict__ ktile_next,
     floatx16 acc[kKb] = {};
     if (HAS_NEXT) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kf[i] = kread(i);
+        for (int i = 0; i < 4; ++i) kf[i] = kf_first[i];
     }
     if (HAS_CUR) {
 #pragma unroll
@@ -602,8 +613,10 @@ struct SplitWs {
 // phase A issues first while the other's pure-MFMA phase B fills the gaps;
 // the planner picks the other instantiation where one heavy query tile sets
 // the kernel's length, since there the default arbitration (the older,
-// heavier work-group first) keeps that tile moving.  A compile-time choice:
-// a run-time branch around the priority changes measured several per cent
+// heavier work-group first) keeps that tile moving.  The same instantiation
+// (a throughput-bound launch) also reads each step's first K fragments
+// before issuing the step's staging loads.  A compile-time choice: a
+// run-time branch around the priority changes measured several per cent
 // slower, as it splits the scheduled step.
 template <int HD, typename TI, typename TO, bool CAUSAL, bool PRIO>
 __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel(
@@ -751,7 +764,9 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     {
         X8 vf_unused[4];
         float l_unused = 0.0f;
-        phase_a<HD, TI, false, true, false, PRIO>(kbuf(0), qb, sa, sa, pb, l_unused, m_ref, c2, l32, g, nullptr,
+        X8 kf[4];
+        load_k_first<HD, TI>(kf, kbuf(0), l32, g);
+        phase_a<HD, TI, false, true, false, PRIO>(kf, kbuf(0), qb, sa, sa, pb, l_unused, m_ref, c2, l32, g, nullptr,
                                             vt_off, vf_unused);
         if (tile_needs_mask<CAUSAL>(t_lo, pos_w, kv_len)) mask_scores<CAUSAL>(sa, t_lo, q_pos, kv_len, g);
         // register i's maximum over the kKb blocks, then over the 16 registers
@@ -780,11 +795,19 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     auto step = [&](int j, TileScores& sc, TileScores& sn) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        // A throughput-bound launch (PRIO) reads the first K fragments before
+        // issuing the staging loads, so their LDS latency overlaps the issue
+        // (1-1.7 % faster there); where one heavy query tile sets the
+        // kernel's length, issuing the staging loads first measured 0.3 %
+        // faster.
+        X8 kf[4];
+        if constexpr (PRIO) load_k_first<HD, TI>(kf, kbuf(j + 1), l32, g);
         if (j + 2 < n_tiles) stage_tile<HD>(k_head, kv_row_bytes, hk, kv_len, kv_row(j + 2), kbuf(j + 2), wave, lane);
         stage_tile<HD>(v_head, kv_row_bytes, hk, kv_len, kv_row(j + 1), vbuf(j + 1), wave, lane);
+        if constexpr (!PRIO) load_k_first<HD, TI>(kf, kbuf(j + 1), l32, g);
         X8 vf[4];
         float l_tile;
-        phase_a<HD, TI, true, true, true, PRIO>(kbuf(j + 1), qb, sc, sn, pb, l_tile, m_ref, c2, l32, g, vbuf(j),
+        phase_a<HD, TI, true, true, true, PRIO>(kf, kbuf(j + 1), qb, sc, sn, pb, l_tile, m_ref, c2, l32, g, vbuf(j),
                                           vt_off, vf);
         if constexpr (kOverflowCheck<HD>) {
             if (__builtin_amdgcn_ballot_w64(!(l_tile <= kSumLimit)))
@@ -802,7 +825,8 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
         __syncthreads();
         X8 vf[4];
         float l_tile;
-        phase_a<HD, TI, true, false, true, PRIO>(nullptr, qb, sc, sc, pb, l_tile, m_ref, c2, l32, g, vbuf(j),
+        X8 kf_unused[4];
+        phase_a<HD, TI, true, false, true, PRIO>(kf_unused, nullptr, qb, sc, sc, pb, l_tile, m_ref, c2, l32, g, vbuf(j),
                                            vt_off, vf);
         if constexpr (kOverflowCheck<HD>) {
             if (__builtin_amdgcn_ballot_w64(!(l_tile <= kSumLimit)))
