@@ -134,7 +134,11 @@ struct Operand<__bf16> {
 // nearest even) and stored with one non-temporal vector store: the output is
 // written once and not read again by the kernel, so it is not kept in the L2
 // (measured 1-2.6 % faster up to 4k tokens, where the f32 output is a large
-// share of the launch's traffic, than ordinary stores).
+// share of the launch's traffic, than ordinary stores).  store4 takes an
+// address (the merge of a split query tile); buffer_store4 a buffer record and
+// an offset, and the hardware drops a store past the record's end, which
+// bounds the rows of the whole-tile epilogue without a branch.  Cache-policy
+// value 2 is the non-temporal bit.
 __device__ __forceinline__ void store4(float* p, floatx4 o) {
     __builtin_nontemporal_store(o, reinterpret_cast<floatx4*>(p));
 }
@@ -145,6 +149,20 @@ __device__ __forceinline__ void store4(_Float16* p, floatx4 o) {
 __device__ __forceinline__ void store4(__bf16* p, floatx4 o) {
     typedef __bf16 b4 __attribute__((ext_vector_type(4)));
     __builtin_nontemporal_store(__builtin_convertvector(o, b4), reinterpret_cast<b4*>(p));
+}
+
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, floatx4 o, float*) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uintx4, o), r, off, 0, 2);
+}
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, floatx4 o, _Float16*) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, __builtin_convertvector(o, h4)), r, off, 0, 2);
+}
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, floatx4 o, __bf16*) {
+    typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, __builtin_convertvector(o, b4)), r, off, 0, 2);
 }
 
 // Per-head-dimension layout of a K/V tile in LDS.
@@ -877,15 +895,27 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
                                    oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv};
                 *reinterpret_cast<floatx4*>(chunk_at(l32, 8 * db + 2 * jj + g)) = o;
             }
-        // The wave reads back what its own lanes wrote.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // The wave reads back what its own lanes wrote (a wave's LDS
+        // accesses complete in order).  The stores go through a buffer
+        // record that ends at the wave's last query row (the formula of
+        // stage_q), so rows past q_len are dropped by the hardware bound and
+        // no store needs a branch; a per-row branch made the compiler wait
+        // for each read-back in turn.
         constexpr int kRowsPerRead = kWaveSize / kRowChunks;
         const int rr = lane / kRowChunks, c = lane % kRowChunks;
+        const uint32_t o_stride = (uint32_t)n_q_heads * HD * (uint32_t)sizeof(TO);
+        const uint32_t o_seg = HD * (uint32_t)sizeof(TO);
+        const int o_rows = q_len - qw;
+        const uint32_t o_records = o_rows >= kQRowsPerWave ? (uint32_t)kQRowsPerWave * o_stride
+                                   : o_rows > 0 ? (uint32_t)o_rows * o_stride - (uint32_t)h * o_seg : 0u;
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<char*>(out) + ((size_t)(uint32_t)qw * n_q_heads + h) * o_seg, (short)0, (int)o_records,
+            kBufferFlags);
 #pragma unroll
         for (int kk = 0; kk < kQRowsPerWave / kRowsPerRead; ++kk) {
             const int r = kk * kRowsPerRead + rr;
             const floatx4 o = *reinterpret_cast<const floatx4*>(chunk_at(r, c));
-            if (qw + r < q_len) store4(out + ((size_t)(qw + r) * n_q_heads + h) * HD + 4 * c, o);
+            buffer_store4(orsrc, (uint32_t)r * o_stride + (uint32_t)c * 4 * (uint32_t)sizeof(TO), o, (TO*)nullptr);
         }
         return;
     }
