@@ -1,5 +1,6 @@
-"""Split launches: rows past q_len are never written, and a merge reads only
-the partial results of its own launch.
+"""Rows past q_len are never written (split launches and the whole-tile
+epilogue of unsplit chunks), and a merge reads only the partial results of its
+own launch.
 
 A split launch (fa_plan.kv_splits > 1) writes per-part partial outputs to a
 workspace and the last part of each query tile merges them.  These tests
@@ -61,6 +62,38 @@ def test_split_guard_band_and_rerun(fa, q_len, kv_len, nq, nkv, types):
     assert torch.equal(first, out), "reruns differ"
     atol, rtol = bar(in_t)
     err = parity_errors(out.float().cpu().numpy(), attention_chunk_f64(q, k, v, SCALE, True), OUT_UNIT[out_t])
+    assert within_tolerance(err, atol, rtol), err
+
+
+UNSPLIT = [
+    # (q_len, kv_len, n_q_heads, n_kv_heads, head_dim): chunks whose plan does
+    # not split, with q_len not a multiple of 32 (waves partly or wholly past
+    # q_len) and several heads (each head's rows start at its own offset)
+    (77, 600, 6, 2, 128),
+    (33, 300, 8, 8, 64),
+    (100, 900, 4, 1, 256),
+    (5, 5, 3, 3, 128),
+]
+
+
+@pytest.mark.parametrize("q_len,kv_len,nq,nkv,hd", UNSPLIT)
+@pytest.mark.parametrize("types", [("f16", "f32"), ("bf16", "bf16"), ("f16", "f16")])
+def test_unsplit_chunk_guard_band(fa, q_len, kv_len, nq, nkv, hd, types):
+    """Whole-tile epilogue of a chunk: rows past q_len stay NaN."""
+    in_t, out_t = types
+    plan = fa.fa_prefill_chunk_plan(nq, nkv, q_len, kv_len, hd, 1)
+    assert plan.kv_splits == 1, "shape chosen not to split"
+    q, k, v = make_custom_inputs(kv_len, nq, nkv, seed=q_len * 7 + hd, q_len=q_len, in_dtype=in_t, head_dim=hd)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[out_t]
+    buf = torch.full((q_len + 40, nq, hd), float("nan"), dtype=tdt, device="cuda")
+    out = buf[:q_len]
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    fa.attention(dq, dk, dv, 1.0 / hd ** 0.5, True, out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[q_len:]).all().item(), "rows past q_len were written"
+    atol, rtol = bar(in_t)
+    ref = attention_chunk_f64(q, k, v, float(np.float32(1.0 / hd ** 0.5)), True)
+    err = parity_errors(out.float().cpu().numpy(), ref, OUT_UNIT[out_t])
     assert within_tolerance(err, atol, rtol), err
 
 
