@@ -53,11 +53,36 @@ STORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_store_kv_traffic.json")
 STORE_ROTATION_BYTES = 1 << 30
 
 
+def code_tokens(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed: what
+    the compiler sees, so that a comment-only edit keeps the hash."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif text[i] == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
+    """Hash of the kernel's code (comments and layout excluded)."""
     h = hashlib.sha256()
     for rel in sources:
-        with open(os.path.join(ROOT, rel), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as fh:
+            h.update(code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

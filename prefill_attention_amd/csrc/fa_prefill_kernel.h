@@ -30,9 +30,13 @@
 //    instruction, and it keeps both read patterns below free of bank
 //    conflicts.
 //
+//  * Each wavefront copies its 32 query rows into LDS the same way (whole
+//    rows, same chunk permutation) and reads its Q^T fragments from there
+//    into registers once.
+//
 //  * Scores are computed transposed, S^T = K Q^T, on the 32x32x16 MFMA
-//    (f16 or bf16 operands): K (from LDS) is the A operand, Q^T (registers,
-//    loaded once) is B.  In the 32x32 accumulator a lane holds one column —
+//    (f16 or bf16 operands): K (from LDS) is the A operand, Q^T (registers)
+//    is B.  In the 32x32 accumulator a lane holds one column —
 //    one query — and 16 of the 32 keys.  So the softmax state of a query
 //    lives in one lane pair (lane, lane^32): row max and row sum are in-lane
 //    reductions plus one v_permlane32_swap, and the probabilities of a lane
@@ -70,9 +74,14 @@
 //  * Work-group order: the heaviest query tiles first; when the head count is
 //    a multiple of 8, the 8 XCDs (which receive work-groups round-robin, so
 //    indices equal mod 8 share one) each own a contiguous range of heads, so
-//    one kv head's K/V stays in one L2,
-//    and an unsplit causal launch reverses the second half of each XCD's
-//    first dispatch wave so that heavy and light query tiles share CUs.
+//    one kv head's K/V stays in one L2, and an unsplit causal launch
+//    reverses the second half of each XCD's first dispatch wave so that heavy
+//    and light query tiles share CUs.
+//
+//  * The output goes through LDS so that each store writes whole rows, and
+//    through a buffer record that ends at the last query row, so rows past
+//    q_len are never written (the pages' tail-stage overrun, "53 · r50",
+//    §3.1).
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -105,3 +105,17 @@ def test_shipped_geometry_and_other_builds_go_elsewhere():
     other = build.geometry_lib_path(32, 4)
     assert other != build.LIB_PATH and os.path.basename(other) == build.LIB_NAME
     assert "kv32_w4" in other
+
+
+def test_kernel_hash_ignores_comments_not_code():
+    """The profile records are keyed by a hash of the kernel's code: comment
+    and layout edits keep it, any token change (also inside a string, such as
+    an inline-asm operand) changes it."""
+    a = 'int f() { // one\n  return 1; /* two */ }\nasm("s_nop 0 // x");\n'
+    b = 'int f() {\n\n  return 1;   }\nasm("s_nop 0 // x"); // three\n'
+    c = 'int f() { return 2; }\nasm("s_nop 0 // x");\n'
+    d = 'int f() { return 1; }\nasm("s_nop 1 // x");\n'
+    assert bench.code_tokens(a) == bench.code_tokens(b)
+    assert bench.code_tokens(a) != bench.code_tokens(c)
+    assert bench.code_tokens(a) != bench.code_tokens(d)
+    assert bench.code_tokens('x = "a\\"b // c"; // d') == 'x = "a\\"b // c";'
