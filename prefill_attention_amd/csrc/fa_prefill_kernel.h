@@ -405,7 +405,10 @@ __device__ __forceinline__ typename Operand<T>::x8 load_vt_slot(const char* vtil
 //     work issued in one slot has no dependency inside it (bitwise the same
 //     values; 1-3 % faster than doing a pair's three steps in one slot).
 //     Register fences pin each step to its slot: the slot barriers alone do
-//     not stop earlier passes from moving pure VALU between slots.
+//     not stop earlier passes from moving pure VALU between slots.  The row-
+//     sum dot products are left unpinned; the compiler gathers them into one
+//     chain after the last MFMA (pinned into the slots they measured 3-10 %
+//     slower).
 // With PREFETCH_V the last four slots also read phase B's first four V^T
 // fragments.  Hard scheduling barriers between slots keep every K read four
 // MFMAs ahead of its use and the exponentials spread under the MFMAs.
