@@ -819,9 +819,9 @@ __global__ __launch_bounds__(kThreads, groups_per_cu(HD)) void fa_prefill_kernel
     // Pipeline step for tile j (its scores in sc), producing the scores of
     // tile j + 1 in sn; with the overflow check the tile's probabilities are
     // checked against kSumLimit before P.V uses them, otherwise phase B also
-    // takes tile j + 1's row maximum for the rescale test.  On entry K(j+1) and V(j) have been
-    // issued; the barrier also frees kbuf(j) and vbuf(j - 1) for K(j+2) and
-    // V(j+1).
+    // takes tile j + 1's row maximum for the rescale test.  On entry K(j+1)
+    // and V(j) have been issued; the barrier also frees kbuf(j) and
+    // vbuf(j - 1) for K(j+2) and V(j+1).
     auto step = [&](int j, TileScores& sc, TileScores& sn) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
